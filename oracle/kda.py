@@ -1,0 +1,116 @@
+"""Float64 token-by-token KDA recurrence (the oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Every array here is
+float64; callers pass the exact values the GPU receives.
+"""
+from __future__ import annotations
+
+import os
+from typing import Optional
+
+import numpy as np
+
+# orkas.ai "Kimi K3 architecture" blog, "A lower bound that deleted a GPU code
+# path": each step may forget down to ~0.67% of a channel and no further;
+# exp(-5) = 0.674%, and 16 steps at the floor give the (-80, 0) tile range.
+LOG_DECAY_FLOOR = -5.0
+
+
+def clamp_log_decay(g: np.ndarray) -> np.ndarray:
+    """g' = min(max(g, -5), 0), elementwise; NaN stays NaN (np.maximum keeps it)."""
+    return np.minimum(np.maximum(np.asarray(g, dtype=np.float64), LOG_DECAY_FLOOR), 0.0)
+
+
+def _step(S, q, k, v, g, beta):
+    """One token for a stack of states.
+
+    S [..., dk, dv]; q, k, g [..., dk]; v [..., dv]; beta [...].  Returns (S', o).
+    """
+    S = np.exp(clamp_log_decay(g))[..., :, None] * S
+    w = np.einsum("...cj,...c->...j", S, k)
+    S = S + beta[..., None, None] * k[..., :, None] * (v - w)[..., None, :]
+    o = np.einsum("...cj,...c->...j", S, q)
+    return S, o
+
+
+def kda_decode_step(state, q, k, v, g, beta):
+    """Single recurrent step: state [N,H,dk,dv] -> (o [N,H,dv], new state)."""
+    S, o = _step(np.asarray(state, np.float64), np.asarray(q, np.float64),
+                 np.asarray(k, np.float64), np.asarray(v, np.float64),
+                 np.asarray(g, np.float64), np.asarray(beta, np.float64))
+    return o, S
+
+
+def kda_forward(q, k, v, g, beta, s0=None, checkpoint_every: int = 0):
+    """Full-sequence KDA, one token at a time.
+
+    q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]; s0: [B,H,dk,dv] or None.
+    Returns (o [B,T,H,dv], final state [B,H,dk,dv], checkpoints) where
+    checkpoints is [B, T // every, H, dk, dv] (the state after tokens
+    every*(j+1)) or None when checkpoint_every == 0.
+    """
+    q, k, v, g, beta = (np.asarray(x, np.float64) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if s0 is None else np.array(s0, dtype=np.float64)
+    o = np.empty((B, T, H, dv))
+    ck = None
+    if checkpoint_every:
+        ck = np.empty((B, T // checkpoint_every, H, dk, dv))
+    for t in range(T):
+        S, o[:, t] = _step(S, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t])
+        if checkpoint_every and (t + 1) % checkpoint_every == 0:
+            ck[:, (t + 1) // checkpoint_every - 1] = S
+    return o, S, ck
+
+
+def _one_head(args):
+    q, k, v, g, beta, s0, every = args
+    o, S, ck = kda_forward(q[None, :, None], k[None, :, None], v[None, :, None],
+                           g[None, :, None], beta[None, :, None], s0[None, None], every)
+    return o[0, :, 0], S[0, 0], None if ck is None else ck[0, :, 0]
+
+
+def kda_forward_heads_parallel(q, k, v, g, beta, s0=None, checkpoint_every: int = 0,
+                               processes: Optional[int] = None):
+    """kda_forward with the independent (b, h) sequences spread over processes.
+
+    Identical arithmetic per head; only the scheduling differs.  Returns the
+    same triple as :func:`kda_forward` and the number of processes used.
+    """
+    q, k, v, g, beta = (np.asarray(x, np.float64) for x in (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if s0 is None:
+        s0 = np.zeros((B, H, dk, dv))
+    jobs = [(q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h], beta[b, :, h], s0[b, h],
+             checkpoint_every) for b in range(B) for h in range(H)]
+    if processes is None:
+        processes = len(os.sched_getaffinity(0))
+    processes = max(1, min(processes, len(jobs)))
+    if processes == 1:
+        res = [_one_head(j) for j in jobs]
+    else:
+        import multiprocessing as mp
+
+        with mp.get_context("fork").Pool(processes) as pool:
+            res = pool.map(_one_head, jobs, chunksize=1)
+    o = np.empty((B, T, H, dv))
+    S = np.empty((B, H, dk, dv))
+    ck = np.empty((B, T // checkpoint_every, H, dk, dv)) if checkpoint_every else None
+    for idx, (oh, Sh, ckh) in enumerate(res):
+        b, h = divmod(idx, H)
+        o[b, :, h] = oh
+        S[b, h] = Sh
+        if ck is not None:
+            ck[b, :, h] = ckh
+    return (o, S, ck), processes
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 in float64 over the whole array."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    return float(num / den) if den > 0 else float(num)
