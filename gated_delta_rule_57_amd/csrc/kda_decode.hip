@@ -1,0 +1,144 @@
+// Single-token KDA recurrent update (decode), one workgroup per (sequence, head).
+//
+// Per (n, h), with S the d_k x d_v float32 state (rows = key channels):
+//   S' = Diag(exp g') S,  a = S'^T k,  b = S'^T q,  u = beta (v - a),
+//   S  <- S' + k u^T,     o = b + (k . q) u          (= S^T q after the write)
+// which is the delta-rule step with KDA's per-channel decay (Towards-AI article
+// on Kimi K3, "Kimi Delta Attention (KDA)"), updated in place as the orkas.ai
+// blog's "The cost is paid in the serving stack" section describes for decoding.
+//
+// The step is bound by HBM: the 64 KiB state of a head is read once and
+// written once.  Each of the 256 threads keeps RPT rows x 4 columns of the
+// state in registers between the read and the write, loaded and stored with
+// 128-bit accesses; consecutive lanes cover consecutive 16-byte pieces of a
+// row, so a wavefront touches 1 KiB of contiguous state per access.  The two
+// column reductions (a and b) go through LDS once.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename TIn, typename TOut, int DK, int DV>
+__global__ void __launch_bounds__(256) decode_step_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const TIn* __restrict__ g, const TIn* __restrict__ beta, float* __restrict__ state,
+    TOut* __restrict__ o, int64_t n_heads_total) {
+  constexpr int NT = 256;
+  constexpr int CG = DV / 4;    // column groups of 4 floats
+  constexpr int RG = NT / CG;   // row groups
+  constexpr int RPT = DK / RG;  // rows per thread
+  static_assert(RPT * RG == DK && CG * RG == NT, "thread layout");
+
+  const int64_t hd = blockIdx.x;
+  if (hd >= n_heads_total) return;
+  const int t = threadIdx.x;
+  const int cg = t % CG;
+  const int rg = t / CG;
+
+  __shared__ float s_q[DK], s_k[DK], s_dec[DK];
+  __shared__ float s_part_a[RG][DV], s_part_b[RG][DV];
+  __shared__ float s_u[DV];
+  __shared__ float s_kq;
+
+  float4* st = reinterpret_cast<float4*>(state + hd * (int64_t)(DK * DV));
+  float4 S[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) S[i] = st[(rg + RG * i) * CG + cg];
+
+  if (t < DK) {
+    const int64_t off = hd * DK + t;
+    s_q[t] = to_f32(q[off]);
+    s_k[t] = to_f32(k[off]);
+    s_dec[t] = exp2_hw(clamp_log_decay(to_f32(g[off])) * kLog2e);
+  }
+  __syncthreads();
+  if (t < 64) {
+    float x = 0.f;
+#pragma unroll
+    for (int c = t; c < DK; c += 64) x += s_q[c] * s_k[c];
+    x = wave_sum(x);
+    if (t == 0) s_kq = x;
+  }
+
+  float4 pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + RG * i;
+    const float d = s_dec[c], kc = s_k[c], qc = s_q[c];
+    S[i].x *= d;
+    S[i].y *= d;
+    S[i].z *= d;
+    S[i].w *= d;
+    pa.x += kc * S[i].x;
+    pa.y += kc * S[i].y;
+    pa.z += kc * S[i].z;
+    pa.w += kc * S[i].w;
+    pb.x += qc * S[i].x;
+    pb.y += qc * S[i].y;
+    pb.z += qc * S[i].z;
+    pb.w += qc * S[i].w;
+  }
+  *reinterpret_cast<float4*>(&s_part_a[rg][4 * cg]) = pa;
+  *reinterpret_cast<float4*>(&s_part_b[rg][4 * cg]) = pb;
+  __syncthreads();
+
+  if (t < DV) {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      a += s_part_a[r][t];
+      b += s_part_b[r][t];
+    }
+    const float bt = to_f32(beta[hd]);
+    const float u = bt * (to_f32(v[hd * DV + t]) - a);
+    s_u[t] = u;
+    o[hd * DV + t] = from_f32<TOut>(b + s_kq * u);
+  }
+  __syncthreads();
+
+  const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int c = rg + RG * i;
+    const float kc = s_k[c];
+    float4 x = S[i];
+    x.x += kc * u4.x;
+    x.y += kc * u4.y;
+    x.z += kc * u4.z;
+    x.w += kc * u4.w;
+    st[c * CG + cg] = x;
+  }
+}
+
+template <typename TIn, typename TOut, int DK, int DV>
+hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, float* state, void* o, int64_t nh,
+                         hipStream_t stream) {
+  decode_step_kernel<TIn, TOut, DK, DV><<<dim3((unsigned)nh), dim3(256), 0, stream>>>(
+      (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, state,
+      (TOut*)o, nh);
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t dispatch_decode_d(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
+                             hipStream_t s) {
+  if (dk == 128 && dv == 128) return launch_decode<TIn, TOut, 128, 128>(q, k, v, g, beta, state, o, nh, s);
+  if (dk == 64 && dv == 64) return launch_decode<TIn, TOut, 64, 64>(q, k, v, g, beta, state, o, nh, s);
+  if (dk == 64 && dv == 128) return launch_decode<TIn, TOut, 64, 128>(q, k, v, g, beta, state, o, nh, s);
+  return launch_decode<TIn, TOut, 128, 64>(q, k, v, g, beta, state, o, nh, s);
+}
+
+hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
+                       bool in_bf16, bool out_bf16, hipStream_t s) {
+  if (in_bf16) {
+    return out_bf16 ? dispatch_decode_d<__bf16, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s)
+                    : dispatch_decode_d<__bf16, float>(q, k, v, g, beta, state, o, nh, dk, dv, s);
+  }
+  return out_bf16 ? dispatch_decode_d<float, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s)
+                  : dispatch_decode_d<float, float>(q, k, v, g, beta, state, o, nh, dk, dv, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,73 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Log-decay floor: each step keeps at least exp(-5) ~ 0.67% of a key channel
+// (orkas.ai blog "Kimi K3 architecture", "A lower bound that deleted a GPU code
+// path").
+constexpr float kLogDecayFloor = -5.0f;
+
+// min(max(g, -5), 0) that keeps NaN (fmaxf/fminf would drop it).
+__device__ __forceinline__ float clamp_log_decay(float g) {
+  return (g != g) ? g : fminf(fmaxf(g, kLogDecayFloor), 0.0f);
+}
+
+// 2^x on the hardware transcendental unit.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Load 8 consecutive elements (16 bytes for bf16, 32 bytes for f32) as floats.
+__device__ __forceinline__ void load8(const __bf16* p, float* out) {
+  bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8(const float* p, float* out) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = a[i];
+    out[4 + i] = b[i];
+  }
+}
+
+// 16 bytes of global input as floats: 8 bfloat16 or 4 float32 values.
+__device__ __forceinline__ void load16(const __bf16* p, float* out) { load8(p, out); }
+__device__ __forceinline__ void load16(const float* p, float* out) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = a[i];
+}
+
+__device__ __forceinline__ void store8(float* p, const float* x) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+// Wave-wide sum (64 lanes).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace kda

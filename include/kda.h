@@ -1,0 +1,130 @@
+/*
+ * kda.h - C ABI of the Kimi Delta Attention (KDA) library for AMD MI355X (gfx950).
+ *
+ * KDA is the fixed-size-state sequence mixer of the Kimi K3 hybrid model.  Per
+ * batch row b and head h it carries a d_k x d_v state S and, for every token t,
+ *
+ *     g'_t = min(max(g_t, -5), 0)                       (per key channel)
+ *     S_t  = (I - beta_t k_t k_t^T) Diag(exp g'_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t  = S_t^T q_t
+ *
+ * Sources (the pages' formulas were lost in extraction; the form above is the
+ * standard one for the lineage they describe):
+ *   - the delta rule -> scalar forget gate -> per-channel ("diagonal") gate
+ *     lineage, and the negative-softplus decay logits: Towards-AI article on the
+ *     Kimi K3 report, section "Kimi Delta Attention (KDA)";
+ *   - the -5 floor on the log-decay (each step keeps at least ~0.67% of a
+ *     channel) and its consequence that a 16-token tile's cumulative log-decay
+ *     stays in [-80, 0], so diagonal tiles of the chunked form run as the same
+ *     dense matrix product as off-diagonal tiles: orkas.ai blog "Kimi K3
+ *     architecture", section "A lower bound that deleted a GPU code path";
+ *   - the in-place recurrent state update of decoding: same blog, section
+ *     "The cost is paid in the serving stack".
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *     row-major and contiguous.  Token tensors are [B, T, H, D]; states are
+ *     [B, H, d_k, d_v] float32 (rows = key channels).
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory, keeps no global mutable state, and never synchronises: work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     execution errors surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-OK status means nothing was enqueued.  KDA_ERR_HIP reports a failed
+ *     launch (hipGetLastError after the enqueue).
+ *   - Supported sizes: d_k, d_v in {64, 128}; chunk == 64; T >= 1.  float32
+ *     inputs support d_k = d_v = 64 (the float32-parity configuration);
+ *     bfloat16 inputs support all four (d_k, d_v) pairs.
+ *   - Pointers must be 16-byte aligned.
+ *   - Concurrent calls on different streams are safe (the library is
+ *     stateless); calls that write the same buffers race.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,      /* a required pointer is NULL */
+  KDA_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
+  KDA_ERR_DTYPE = -3,     /* unsupported dtype combination */
+  KDA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+  KDA_ERR_WORKSPACE = -5, /* workspace missing or too small */
+  KDA_ERR_ALIAS = -6,     /* an output overlaps an input it may not overlap */
+  KDA_ERR_HIP = -7        /* the HIP runtime reported an error at launch */
+} kda_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_str(kda_status_t status);
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
+ * Returns 0 as well for unsupported sizes; kda_chunk_fwd then reports why. */
+size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+                                     kda_dtype_t in);
+
+/*
+ * kda_chunk_fwd - chunked parallel forward (prefill) over whole sequences.
+ *
+ * Computes o_t for t = 0..T-1 and the state after token T for every (b, h),
+ * starting from `initial_state`, by the recurrence above, evaluated in chunks
+ * of `chunk` tokens (the chunk-parallel rewrite the Towards-AI article's "Kimi
+ * Delta Attention (KDA)" section names as the usual linear-attention layout).
+ *
+ *   q, k          [B, T, H, dk]  dtype `in`   query / key (not normalised here)
+ *   v             [B, T, H, dv]  dtype `in`
+ *   g             [B, T, H, dk]  dtype `in`   log-decay (clamped to [-5, 0]
+ *                                             here; NaN propagates)
+ *   beta          [B, T, H]      dtype `in`   write strength, used as given
+ *   initial_state [B, H, dk, dv] float32      NULL = zeros
+ *   o             [B, T, H, dv]  dtype `out`  written
+ *   final_state   [B, H, dk, dv] float32      written; NULL = not wanted.
+ *                                             May equal initial_state exactly
+ *                                             (in-place update); any other
+ *                                             overlap is KDA_ERR_ALIAS.
+ *   checkpoints   [B, T / checkpoint_every, H, dk, dv] float32, or NULL.
+ *                 Entry j is the state after token checkpoint_every*(j+1).
+ *   checkpoint_every  0 = off; else a positive multiple of `chunk`.
+ *   workspace / workspace_bytes  at least kda_chunk_fwd_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0).
+ *
+ * T need not be a multiple of `chunk`: the tail is padded inside the kernel
+ * with beta = 0, g = 0 tokens, which leave the state unchanged.
+ */
+kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* initial_state, void* o,
+                           float* final_state, float* checkpoints, int64_t checkpoint_every,
+                           int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+                           kda_dtype_t in, kda_dtype_t out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * kda_recurrent_step - one decode step for N independent sequences.
+ *
+ * For every (n, h): S <- Diag(exp g') S; S <- S + beta k (v - S^T k)^T;
+ * o = S^T q.  The state is updated IN PLACE (no copy is kept, so a step
+ * cannot be undone; the orkas.ai blog's "The cost is paid in the serving
+ * stack" section describes this property of KDA decoding).
+ *
+ *   q, k, g  [N, H, dk]      dtype `in`
+ *   v        [N, H, dv]      dtype `in`
+ *   beta     [N, H]          dtype `in`
+ *   state    [N, H, dk, dv]  float32, read and overwritten
+ *   o        [N, H, dv]      dtype `out`, must not overlap `state`
+ */
+kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, const void* g,
+                                const void* beta, float* state, void* o, int64_t N, int64_t H,
+                                int dk, int dv, kda_dtype_t in, kda_dtype_t out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
