@@ -1,0 +1,176 @@
+"""Throughput of the KDA hot path on one MI355X, printed as one JSON line.
+
+A step is one kda_chunk_fwd (chunked prefill) over the 4 x 4096-token, 32-head,
+d = 128 bfloat16 workload with a float32 initial state, inputs resident in HBM.
+The same run also times kda_recurrent_step on the 256-sequence decode workload
+(1000 chained steps) and the float64 CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode-step HBM GB/s (% peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6
+
+
+def prefill_flops_per_token_head(dk: int, dv: int, C: int = 64) -> float:
+    """State products + block-triangular intra-chunk products (dense 16-tiles) + UT solve."""
+    return 6 * dk * dv + 2 * C * (10 / 16) * (3 * dk + 2 * dv) + (2 / 3) * C * C
+
+
+def prefill_bytes(B, T, H, dk, dv, in_bytes=2, out_bytes=2) -> float:
+    """q, k, g, v, beta read once; o written once; state read and written once."""
+    per_tok = (3 * dk + dv + 1) * in_bytes + dv * out_bytes
+    return B * T * H * per_tok + 2 * B * H * dk * dv * 4
+
+
+def decode_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2) -> float:
+    per_head = 2 * dk * dv * 4 + (3 * dk + dv + 1) * in_bytes + dv * out_bytes
+    return N * H * per_head
+
+
+def time_prefill(kda, torch, w, steps, warmup):
+    import synth
+
+    d = synth.device_prefill_inputs(w, "cuda")
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device="cuda")
+    sf = torch.empty_like(d["s0"])
+
+    def step():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], o=o,
+                          final_state=sf)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert bool(torch.isfinite(o.float()).all()), "non-finite prefill output"
+    return ms
+
+
+def time_decode(kda, torch, w, steps, warmup):
+    import synth
+
+    d = synth.device_decode_inputs(w, steps, "cuda")
+    state = d["s0"].clone()
+    o = torch.empty((w.B, w.H, w.dv), dtype=d["q"].dtype, device="cuda")
+
+    def step(s):
+        kda.kda_recurrent_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], state,
+                               o=o)
+
+    for s in range(warmup):
+        step(s % steps)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    assert bool(torch.isfinite(state).all()), "non-finite decode state"
+    return us
+
+
+def cpu_baseline(w, sample_heads: int):
+    """The float64 oracle on the first `sample_heads` (b, h) sequences of the workload."""
+    import oracle
+    import synth
+
+    x = synth.prefill_inputs(w.replace(B=1))
+    sl = slice(0, sample_heads)
+    args = [x[n][:, :, sl] for n in ("q", "k", "v", "g", "beta")]
+    t = time.perf_counter()
+    procs = min(16, len(os.sched_getaffinity(0)))
+    _, procs = oracle.kda_forward_heads_parallel(*args, x["s0"][:, sl], processes=procs)
+    dt = time.perf_counter() - t
+    token_heads = sample_heads * w.T
+    return {"value": token_heads / w.H / dt, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+            "sample": f"{sample_heads} of the {w.B * w.H} (batch, head) sequences x {w.T} tokens "
+                      f"({token_heads} token-heads, {dt:.1f} s wall); tokens/s counts a token "
+                      f"as all {w.H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the KDA path here has "
+              "no multi-GPU leg", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_57_amd as kda
+    import synth
+
+    w = synth.PREFILL_B4_T4096
+    ms = time_prefill(kda, torch, w, args.steps, args.warmup)
+    toks = w.B * w.T
+    flops = prefill_flops_per_token_head(w.dk, w.dv) * toks * w.H
+    nbytes = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": toks / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "inputs": "bf16", "state": "f32", "output": "bf16",
+                   "decay_logits": "N(0,2)"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel<bf16,bf16,128,128,64,4>",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_decode:
+        wd = synth.DECODE_N256
+        us = time_decode(kda, torch, wd, args.decode_steps, 10)
+        db = decode_bytes(wd.B, wd.H, wd.dk, wd.dv)
+        dgbs = db / (us * 1e-6) / 1e9
+        line["decode"] = {"workload": wd.name, "us_per_step": us, "steps_timed": args.decode_steps,
+                          "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                                       "traffic": None,
+                                       "kernel": "decode_step_kernel<bf16,bf16,128,128>",
+                                       "algorithmic_bytes_per_launch": db}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,6 +28,15 @@
 // itself) and U are carried as hi + lo bfloat16 pairs (three products per
 // pair of split operands); A, T, W, (q 2^G), S and the state-update key
 // operand are single bfloat16.  float32 inputs use the float32 MFMA throughout.
+//
+// Schedule of one chunk (eight waves, two per SIMD; wave w owns row tile w%4 of
+// the chunk for half of the value-column tiles, and a fixed set of state
+// tiles; "|" = barrier):
+//   stage prefetched inputs, prefetch the next chunk | sub-tile scans (one
+//   thread per channel and token range) | operands | A and P tile pairs |
+//   diagonal 16x16 inverses, (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8) on MFMA
+//   from registers | three block-substitution levels | per row tile: W, U0,
+//   U = U0 - W S, Qc S | P U, output, state update | state to its MFMA operand.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -58,6 +67,18 @@ struct Mfma<false> {
   __device__ static __forceinline__ frag ld(const op_t* p) { return *p; }
 };
 
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Z = X Y for 16x16 float32 matrices held in the MFMA result layout (lane l
+// holds rows 4*(l>>4)+m, column l&15).  X is passed transposed (Xt), Y as is:
+// in that form both are already the operands of the k-steps, no data movement.
+__device__ __forceinline__ f32x4 mm16(const f32x4& Xt, const f32x4& Y, f32x4 acc) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) acc = mma_f32(Xt[kb], Y[kb], acc);
+  return acc;
+}
 
 constexpr int kC = 64;    // chunk
 constexpr int kSub = 16;  // sub-tile
@@ -83,47 +104,54 @@ struct PrefillLayout {
   static constexpr int SZ_TB = kC * LDC * OPB;
   static constexpr int SZ_UT = (BF16 ? 2 : 1) * DVS * LDC * OPB;
   static constexpr int PH1 = 2 * SZ_K + SZ_Q2 + SZ_L;
-  static constexpr int PH2 = 2 * SZ_KCT + SZ_QC + SZ_TF + SZ_TB;
+  static constexpr int PH2 = 2 * SZ_KCT + SZ_QC + SZ_TB + SZ_TF;
   static constexpr int REGION = PH1 > PH2 ? PH1 : PH2;
-  // phase-1 view of the shared region
+  // phase-1 view of the shared region: raw inputs, then the A/P operands
   static constexpr int O_K = 0, O_Q = SZ_K, O_Q2 = 2 * SZ_K, O_L = 2 * SZ_K + SZ_Q2;
-  // phase-2 view: dead-first order so U^T can reuse KcT | Tf | Tb
-  static constexpr int O_KCT = 0, O_TF = SZ_KCT, O_TB = SZ_KCT + SZ_TF;
-  static constexpr int O_QC = O_TB + SZ_TB, O_KBT = O_QC + SZ_QC;
-  static constexpr int O_UT = 0;
-  static_assert(SZ_UT <= SZ_KCT + SZ_TF + SZ_TB, "U^T must fit in the dead prefix");
-  // persistent / per-chunk buffers outside the region
+  // phase-2 view: T float32 last, so that U^T can take its place (and the slack)
+  static constexpr int O_KCT = 0, O_TB = SZ_KCT, O_QC = O_TB + SZ_TB, O_KBT = O_QC + SZ_QC;
+  static constexpr int O_TF = O_KBT + SZ_KCT;
+  static constexpr int O_UT = O_TF;
+  static_assert(O_UT + SZ_UT <= REGION, "U^T must fit over T and the slack");
+  // buffers outside the region
   static constexpr int SZ_AW = (kC * LDA * 4 > kC * LDK * OPB) ? kC * LDA * 4 : kC * LDK * OPB;
   static constexpr int O_A = REGION;  // A, then W
   static constexpr int O_P = O_A + SZ_AW;
   static constexpr int O_VT = O_P + kC * LDA * 4;
   static constexpr int O_ST = O_VT + DVS * LDC * OPB;
   static constexpr int O_SM = O_ST + DVS * LDK * OPB;
-  // small float32 arrays: beta[64], tau[4][DK], eref[4][DK], ebar[4][DK], pair[6][DK], egam[DK]
-  static constexpr int SM_BETA = 0, SM_TAU = 64, SM_EREF = 64 + 4 * DK, SM_EBAR = 64 + 8 * DK;
-  static constexpr int SM_PAIR = 64 + 12 * DK, SM_EGAM = 64 + 18 * DK;
-  static constexpr int SZ_SM = (64 + 19 * DK) * 4;
+  // small float32 arrays: beta[64], tau[4][DK], pair[6][DK], egam[DK]
+  static constexpr int SM_BETA = 0, SM_TAU = 64, SM_PAIR = 64 + 4 * DK, SM_EGAM = 64 + 10 * DK;
+  static constexpr int SZ_SM = (64 + 11 * DK) * 4;
   static constexpr int TOTAL = O_SM + SZ_SM;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-template <typename TIn, typename TOut, int DK, int DV, int DVS, int NW>
-__global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
+template <typename TIn, typename TOut, int DK, int DV, int DVS>
+__global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   typedef PrefillLayout<TIn, DK, DVS> Lay;
   constexpr bool BF16 = Lay::BF16;
   typedef Mfma<BF16> M;
   typedef typename M::op_t op_t;
   typedef typename M::frag frag;
-  constexpr int NT = NW * 64;
+  constexpr int NW = 8, NT = 512;
   constexpr int KS = M::KSTEP, KPL = M::KPL;
   constexpr int LDK = Lay::LDK, LDC = Lay::LDC, LDF = Lay::LDF, LDA = Lay::LDA;
   constexpr int NSLICE = DV / DVS;
-  constexpr int NST = (DK / 16) * (DVS / 16);  // state tiles
-  constexpr int NSW = NST / NW;
-  constexpr int NU = (kC / 16) * (DVS / 16);  // U / O tiles
-  constexpr int NUW = (NU + NW - 1) / NW;
-  static_assert(NST % NW == 0, "state tiles per wave");
-  static_assert(NW >= 4, "the sub-tile solve uses four waves");
+  constexpr int NJT = DVS / 16;          // value-column tiles
+  constexpr int NJW = NJT / 2;           // value-column tiles per wave (two waves per row tile)
+  constexpr int NST = (DK / 16) * NJT;   // state tiles
+  constexpr int SPW = NST / NW;          // state tiles per wave
+  constexpr int NH = (NT / DK) < 4 ? NT / DK : 4;  // threads per channel (channel-major phases)
+  constexpr int NCM = NH * DK;           // active channel-major threads
+  constexpr int RPC = kC / NH;           // tokens per channel-major thread
+  constexpr int SPT = RPC / kSub;        // sub-tiles per channel-major thread
+  constexpr int E16 = 16 / sizeof(TIn);  // input elements per 16-byte load
+  constexpr int NPF = kC * DK / E16 / NT;
+  constexpr int NVP = kC * DVS / E16;    // 16-byte pieces of v per chunk
+  constexpr int NPV = (NVP + NT - 1) / NT;
+  static_assert(NPF * E16 * NT == kC * DK, "load layout");
+  static_assert(SPW * NW == NST && NJW >= 1 && SPT >= 1 && NCM <= NT, "layout");
 
   extern __shared__ __align__(16) unsigned char smem[];
   op_t* sK = reinterpret_cast<op_t*>(smem + Lay::O_K);
@@ -131,10 +159,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
   op_t* sQ2 = reinterpret_cast<op_t*>(smem + Lay::O_Q2);
   float* sL = reinterpret_cast<float*>(smem + Lay::O_L);
   op_t* sKcT = reinterpret_cast<op_t*>(smem + Lay::O_KCT);
-  float* sTf = reinterpret_cast<float*>(smem + Lay::O_TF);
   op_t* sTb = reinterpret_cast<op_t*>(smem + Lay::O_TB);
   op_t* sQc = reinterpret_cast<op_t*>(smem + Lay::O_QC);
   op_t* sKbT = reinterpret_cast<op_t*>(smem + Lay::O_KBT);
+  float* sTf = reinterpret_cast<float*>(smem + Lay::O_TF);
   op_t* sUT = reinterpret_cast<op_t*>(smem + Lay::O_UT);
   op_t* sUT2 = sUT + DVS * LDC;  // lo part (bf16 only)
   float* sA = reinterpret_cast<float*>(smem + Lay::O_A);
@@ -145,8 +173,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
   float* sm = reinterpret_cast<float*>(smem + Lay::O_SM);
   float* sBeta = sm + Lay::SM_BETA;
   float* sTau = sm + Lay::SM_TAU;
-  float* sERef = sm + Lay::SM_EREF;
-  float* sEBar = sm + Lay::SM_EBAR;
   float* sPair = sm + Lay::SM_PAIR;
   float* sEGam = sm + Lay::SM_EGAM;
 
@@ -156,6 +182,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int kofs = lg * KPL;
+  const int rt = wave & 3;       // row tile of the chunk owned by this wave
+  const int jt0 = (wave >> 2) * NJW;  // its first value-column tile
 
   // Workgroup -> (head, slice): consecutive workgroups are dealt round-robin to
   // the 8 XCDs, so give all slices of a head the same XCD (and L2).
@@ -178,24 +206,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
   TOut* go = reinterpret_cast<TOut*>(p.o);
   const int64_t state_off = head * (int64_t)DK * DV;
 
-  // ---- state slice in accumulators (D layout: row 4*lg+m, col l16 of a 16x16 tile)
-  f32x4 Sacc[NSW];
+  // ---- state slice in accumulators: tiles tt = SPW*wave + i -> (ct, jt)
+  f32x4 Sacc[SPW];
 #pragma unroll
-  for (int i = 0; i < NSW; ++i) {
-    const int tt = wave + NW * i;
-    const int ct = tt / (DVS / 16), jt = tt % (DVS / 16);
+  for (int i = 0; i < SPW; ++i) {
+    const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int c = 16 * ct + 4 * lg + m, jv = 16 * jt + l16;
       Sacc[i][m] = p.s0 ? p.s0[state_off + (int64_t)c * DV + j0 + jv] : 0.f;
     }
   }
-
   auto store_state_operand = [&]() {
 #pragma unroll
-    for (int i = 0; i < NSW; ++i) {
-      const int tt = wave + NW * i;
-      const int ct = tt / (DVS / 16), jt = tt % (DVS / 16);
+    for (int i = 0; i < SPW; ++i) {
+      const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
       op_t* dst = sST + (16 * jt + l16) * LDK + 16 * ct + 4 * lg;
 #pragma unroll
       for (int m = 0; m < 4; ++m) dst[m] = from_f32<op_t>(Sacc[i][m]);
@@ -203,124 +228,134 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
   };
   store_state_operand();
 
+  // ---- register prefetch of one chunk of raw inputs (16-byte pieces)
+  float4 pk[NPF], pq[NPF], pg[NPF], pv[NPV];
+  float pbeta = 0.f;
+  auto prefetch = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int pc = tid + NT * i;
+      const int r = pc / (DK / E16), c = (pc % (DK / E16)) * E16;
+      const int64_t t = t0 + r;
+      if (t < T) {
+        const int64_t off = ((b * T + t) * H + h) * DK + c;
+        pk[i] = *reinterpret_cast<const float4*>(gk + off);
+        pq[i] = *reinterpret_cast<const float4*>(gq + off);
+        pg[i] = *reinterpret_cast<const float4*>(gg + off);
+      } else {
+        pk[i] = pq[i] = pg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int pc = tid + NT * i;
+      const int r = pc / (DVS / E16), jv = (pc % (DVS / E16)) * E16;
+      const int64_t t = t0 + r;
+      pv[i] = (pc < NVP && t < T)
+                  ? *reinterpret_cast<const float4*>(gv + ((b * T + t) * H + h) * DV + j0 + jv)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < kC) pbeta = (t0 + tid < T) ? to_f32(gb[(b * T + t0 + tid) * H + h]) : 0.f;
+  };
+
   const int64_t nchunks = (T + kC - 1) / kC;
-  constexpr int E16 = 16 / sizeof(TIn);  // input elements per 16-byte load
-  constexpr int CGP = DK / 8;            // prep: groups of 8 channels
-  constexpr int RP = NT / CGP;           // prep: rows per pass
-  constexpr int NP = kC / RP;            // prep: passes
-  static_assert(NP * RP == kC, "prep layout");
+  prefetch(0);
 
   for (int64_t n = 0; n < nchunks; ++n) {
     const int64_t t0 = n * kC;
-    // ---- step 0: stage the chunk (k, q raw; g -> gamma; v^T; beta)
-    for (int pc = tid; pc < kC * DK / E16; pc += NT) {
+    // ---- stage the prefetched chunk: k, q raw; g -> gamma (float32); v^T; beta
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int pc = tid + NT * i;
       const int r = pc / (DK / E16), c = (pc % (DK / E16)) * E16;
-      const int64_t t = t0 + r;
+      *reinterpret_cast<float4*>(sK + r * LDK + c) = pk[i];
+      *reinterpret_cast<float4*>(sQ + r * LDK + c) = pq[i];
       float gf[E16];
-      if (t < T) {
-        const int64_t off = ((b * T + t) * H + h) * DK + c;
-        *reinterpret_cast<float4*>(sK + r * LDK + c) = *reinterpret_cast<const float4*>(gk + off);
-        *reinterpret_cast<float4*>(sQ + r * LDK + c) = *reinterpret_cast<const float4*>(gq + off);
-        load16(gg + off, gf);
+      load16(reinterpret_cast<const TIn*>(&pg[i]), gf);
 #pragma unroll
-        for (int e = 0; e < E16; ++e) gf[e] = clamp_log_decay(gf[e]) * kLog2e;
+      for (int e = 0; e < E16; ++e) gf[e] = clamp_log_decay(gf[e]) * kLog2e;
+      if constexpr (E16 == 8) {
+        store8(sL + r * LDF + c, gf);
       } else {
-        *reinterpret_cast<float4*>(sK + r * LDK + c) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(sQ + r * LDK + c) = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int e = 0; e < E16; ++e) gf[e] = 0.f;
+        *reinterpret_cast<f32x4*>(sL + r * LDF + c) = f32x4{gf[0], gf[1], gf[2], gf[3]};
       }
-#pragma unroll
-      for (int e = 0; e < E16; ++e) sL[r * LDF + c + e] = gf[e];
     }
-    for (int pc = tid; pc < kC * DVS / E16; pc += NT) {
-      const int r = pc / (DVS / E16), jv = (pc % (DVS / E16)) * E16;
-      const int64_t t = t0 + r;
-      float vf[E16];
-      if (t < T) {
-        load16(gv + ((b * T + t) * H + h) * DV + j0 + jv, vf);
-      } else {
 #pragma unroll
-        for (int e = 0; e < E16; ++e) vf[e] = 0.f;
-      }
+    for (int i = 0; i < NPV; ++i) {
+      const int pc = tid + NT * i;
+      if (pc >= NVP) break;
+      const int r = pc / (DVS / E16), jv = (pc % (DVS / E16)) * E16;
+      float vf[E16];
+      load16(reinterpret_cast<const TIn*>(&pv[i]), vf);
 #pragma unroll
       for (int e = 0; e < E16; ++e) sVT[(jv + e) * LDC + r] = from_f32<op_t>(vf[e]);
     }
-    if (tid < kC) {
-      const int64_t t = t0 + tid;
-      sBeta[tid] = (t < T) ? to_f32(gb[(b * T + t) * H + h]) : 0.f;
-    }
+    if (tid < kC) sBeta[tid] = pbeta;
+    if (n + 1 < nchunks) prefetch(t0 + kC);
     __syncthreads();
 
-    // ---- step 1: sub-tile cumulative log-decay and per-(sub-tile, channel) factors
-    for (int pr = tid; pr < kNSub * DK; pr += NT) {
-      const int c = pr % DK, R = pr / DK;
+    // ---- sub-tile cumulative log-decay: one thread per (channel, token range)
+    const int cc = tid % DK, hh = tid / DK, r0 = RPC * hh;
+    const bool cm = tid < NCM;  // this thread takes part in the channel-major phases
+    float Lr[RPC];
+#pragma unroll
+    for (int s = 0; s < SPT && cm; ++s) {
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < kSub; ++j) {
-        float* e = sL + (kSub * R + j) * LDF + c;
-        acc += *e;
-        *e = acc;
+        acc += sL[(r0 + kSub * s + j) * LDF + cc];
+        Lr[kSub * s + j] = acc;
       }
-      sTau[R * DK + c] = acc;
-    }
-    __syncthreads();
-    for (int c = tid; c < DK; c += NT) {
-      const float t0_ = sTau[c], t1 = sTau[DK + c], t2 = sTau[2 * DK + c], t3 = sTau[3 * DK + c];
-      sERef[c] = 1.f;
-      sERef[DK + c] = exp2_hw(t0_);
-      sERef[2 * DK + c] = exp2_hw(t0_ + t1);
-      sERef[3 * DK + c] = exp2_hw(t0_ + t1 + t2);
-      sEBar[3 * DK + c] = exp2_hw(t3);
-      sEBar[2 * DK + c] = exp2_hw(t2 + t3);
-      sEBar[DK + c] = exp2_hw(t1 + t2 + t3);
-      sEBar[c] = exp2_hw(t0_ + t1 + t2 + t3);
-      sEGam[c] = exp2_hw(t0_ + t1 + t2 + t3);
-      // pair (R, I < R) -> index R(R-1)/2 + I, factor 2^(sum_{J=I}^{R-1} tau_J)
-      sPair[0 * DK + c] = exp2_hw(t0_);            // (1,0)
-      sPair[1 * DK + c] = exp2_hw(t0_ + t1);       // (2,0)
-      sPair[2 * DK + c] = exp2_hw(t1);             // (2,1)
-      sPair[3 * DK + c] = exp2_hw(t0_ + t1 + t2);  // (3,0)
-      sPair[4 * DK + c] = exp2_hw(t1 + t2);        // (3,1)
-      sPair[5 * DK + c] = exp2_hw(t2);             // (3,2)
+      sTau[(r0 / kSub + s) * DK + cc] = acc;
     }
     __syncthreads();
 
-    // ---- step 2: operands. In place: k -> k 2^L, q -> q 2^L (hi), L -> k 2^-L.
-    // The chunk-relative operands are kept in registers until the A/P products
-    // have released the shared region.
+    // ---- operands (same thread, same elements, so the updates are in place)
     typedef op_t vec8 __attribute__((ext_vector_type(8)));
-    vec8 dKc[NP], dQc[NP], dKb[NP];
+    vec8 dKc[RPC / 8], dQc[RPC / 8], dKb[RPC / 8];
+    if (cm) {
+      float tau[kNSub];
 #pragma unroll
-    for (int mm = 0; mm < NP; ++mm) {
-      const int r = tid / CGP + RP * mm, c0 = 8 * (tid % CGP), R = r / kSub;
-      float kf[8], qf[8], lf[8];
-      load8(sK + r * LDK + c0, kf);
-      load8(sQ + r * LDK + c0, qf);
-      load8(sL + r * LDF + c0, lf);
-      vec8 vkr, vqh, vql;
-      float kd[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ep = exp2_hw(lf[e]), em = exp2_hw(-lf[e]);
-        const float kr = kf[e] * ep, qr = qf[e] * ep;
-        kd[e] = kf[e] * em;
-        vkr[e] = from_f32<op_t>(kr);
-        vqh[e] = from_f32<op_t>(qr);
-        vql[e] = from_f32<op_t>(qr - to_f32(vqh[e]));
-        const float er = sERef[R * DK + c0 + e], eb = sEBar[R * DK + c0 + e];
-        dKc[mm][e] = from_f32<op_t>(kr * er);
-        dQc[mm][e] = from_f32<op_t>(qr * er);
-        dKb[mm][e] = from_f32<op_t>(kd[e] * eb);
+      for (int R = 0; R < kNSub; ++R) tau[R] = sTau[R * DK + cc];
+      if (hh == 0) {
+        sPair[0 * DK + cc] = exp2_hw(tau[0]);                    // (1,0)
+        sPair[1 * DK + cc] = exp2_hw(tau[0] + tau[1]);           // (2,0)
+        sPair[2 * DK + cc] = exp2_hw(tau[1]);                    // (2,1)
+        sPair[3 * DK + cc] = exp2_hw(tau[0] + tau[1] + tau[2]);  // (3,0)
+        sPair[4 * DK + cc] = exp2_hw(tau[1] + tau[2]);           // (3,1)
+        sPair[5 * DK + cc] = exp2_hw(tau[2]);                    // (3,2)
+        sEGam[cc] = exp2_hw(tau[0] + tau[1] + tau[2] + tau[3]);
       }
-      *reinterpret_cast<vec8*>(sK + r * LDK + c0) = vkr;
-      *reinterpret_cast<vec8*>(sQ + r * LDK + c0) = vqh;
-      if constexpr (BF16) *reinterpret_cast<vec8*>(sQ2 + r * LDK + c0) = vql;
-      store8(sL + r * LDF + c0, kd);
+#pragma unroll
+      for (int s = 0; s < SPT; ++s) {
+        const int R = r0 / kSub + s;
+        float ref = 0.f, suf = 0.f;
+#pragma unroll
+        for (int J = 0; J < kNSub; ++J) {
+          if (J < R) ref += tau[J];
+          if (J >= R) suf += tau[J];
+        }
+        const float eref = exp2_hw(ref), ebar = exp2_hw(suf);
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+          const int r = r0 + kSub * s + j, e = kSub * s + j;
+          const float kf = to_f32(sK[r * LDK + cc]), qf = to_f32(sQ[r * LDK + cc]);
+          const float ep = exp2_hw(Lr[e]), em = exp2_hw(-Lr[e]);
+          const float kr = kf * ep, qr = qf * ep, kd = kf * em;
+          sK[r * LDK + cc] = from_f32<op_t>(kr);
+          const op_t qh = from_f32<op_t>(qr);
+          sQ[r * LDK + cc] = qh;
+          if constexpr (BF16) sQ2[r * LDK + cc] = from_f32<op_t>(qr - to_f32(qh));
+          sL[r * LDF + cc] = kd;
+          dKc[e / 8][e % 8] = from_f32<op_t>(kr * eref);
+          dQc[e / 8][e % 8] = from_f32<op_t>(qr * eref);
+          dKb[e / 8][e % 8] = from_f32<op_t>(kd * ebar);
+        }
+      }
     }
     __syncthreads();
 
-    // ---- step 3: A and P tiles, every tile pair one dense product
+    // ---- A and P tiles, every tile pair one dense product
     for (int pi = wave; pi < 10; pi += NW) {
       // pair order (R, I): (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
       const int R = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
@@ -328,7 +363,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
       const float* pair = (I < R) ? sPair + (R * (R - 1) / 2 + I) * DK : nullptr;
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
       const int row = kSub * R + l16, col = kSub * I + l16;
-#pragma unroll 2
+#pragma unroll 1
       for (int kk = 0; kk < DK; kk += KS) {
         const int k0 = kk + kofs;
         const frag aK = M::ld(sK + row * LDK + k0);
@@ -346,9 +381,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
           frag bh, bl;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const __bf16 hh = (__bf16)cf[e];
-            bh[e] = hh;
-            bl[e] = (__bf16)(cf[e] - (float)hh);
+            const __bf16 hh_ = (__bf16)cf[e];
+            bh[e] = hh_;
+            bl[e] = (__bf16)(cf[e] - (float)hh_);
           }
           accA = M::mma(aK, bh, accA);
           accP = M::mma(aQ, bh, accP);
@@ -379,169 +414,167 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
-    // deferred operands into the released region
+    // ---- deferred operands into the released region (channel-major threads):
+    // k 2^G and k 2^(G_end - G) transposed (token-contiguous), q 2^G row-major.
 #pragma unroll
-    for (int mm = 0; mm < NP; ++mm) {
-      const int r = tid / CGP + RP * mm, c0 = 8 * (tid % CGP);
-      *reinterpret_cast<vec8*>(sQc + r * LDK + c0) = dQc[mm];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sKcT[(c0 + e) * LDC + r] = dKc[mm][e];
-        sKbT[(c0 + e) * LDC + r] = dKb[mm][e];
+    for (int e = 0; e < RPC && cm; e += 8) {
+      const vec8 vc = dKc[e / 8], vb = dKb[e / 8];
+      if constexpr (BF16) {
+        *reinterpret_cast<vec8*>(sKcT + cc * LDC + r0 + e) = vc;
+        *reinterpret_cast<vec8*>(sKbT + cc * LDC + r0 + e) = vb;
+      } else {
+        *reinterpret_cast<f32x4*>(sKcT + cc * LDC + r0 + e) = f32x4{vc[0], vc[1], vc[2], vc[3]};
+        *reinterpret_cast<f32x4*>(sKcT + cc * LDC + r0 + e + 4) = f32x4{vc[4], vc[5], vc[6], vc[7]};
+        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e) = f32x4{vb[0], vb[1], vb[2], vb[3]};
+        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e + 4) = f32x4{vb[4], vb[5], vb[6], vb[7]};
       }
     }
-
-    // ---- step 4: T = (I + A)^-1 (float32).  4a: the four 16x16 diagonal blocks
-    if (wave < 4) {
-      const int R = wave;
-      float X[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) X[m] = (4 * lg + m == l16) ? 1.f : 0.f;
-#pragma unroll
-      for (int i = 0; i < kSub - 1; ++i) {
-        const float xi = __shfl(X[i & 3], l16 + 16 * (i >> 2), 64);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = 4 * lg + m;
-          if (r > i) X[m] -= sA[(kSub * R + r) * LDA + kSub * R + i] * xi;
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = kSub * R + 4 * lg + m;
-        sTf[r * LDA + kSub * R + l16] = X[m];
-      }
-    }
-    for (int e = tid; e < 6 * 256; e += NT) {  // zero the blocks above the diagonal
+    for (int e = 0; e < RPC && cm; ++e) sQc[(r0 + e) * LDK + cc] = dQc[e / 8][e % 8];
+    for (int e = tid; e < 6 * 256; e += NT) {  // T' is lower triangular
       const int u = e / 256, w = e % 256;
       const int R = u < 3 ? 0 : u < 5 ? 1 : 2;
       const int I = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
-      sTf[(kSub * R + w / 16) * LDA + kSub * I + w % 16] = 0.f;
+      sTb[(kSub * R + w / 16) * LDC + kSub * I + w % 16] = from_f32<op_t>(0.f);
+    }
+
+    // ---- T = (I + A)^-1.  Diagonal blocks: wave R < 4 inverts I + A_RR in registers.
+    if (wave < kNSub) {
+      const int R = wave;
+      f32x4 Nd, Nt, Id;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        Nd[m] = sA[(kSub * R + 4 * lg + m) * LDA + kSub * R + l16];
+        Nt[m] = sA[(kSub * R + l16) * LDA + kSub * R + 4 * lg + m];
+        Id[m] = (4 * lg + m == l16) ? 1.f : 0.f;
+      }
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 N2 = mm16(Nt, Nd, z), N2t = mm16(Nd, Nt, z);
+      const f32x4 N4 = mm16(N2t, N2, z), N4t = mm16(N2, N2t, z);
+      const f32x4 N8 = mm16(N4t, N4, z);
+      const f32x4 X1 = Id - Nd, X1t = Id - Nt;
+      const f32x4 X2 = mm16(X1t, N2, X1), X2t = mm16(N2, X1t, X1t);
+      const f32x4 X3 = mm16(X2t, N4, X2), X3t = mm16(N4, X2t, X2t);
+      const f32x4 D = mm16(X3t, N8, X3);
+      const float bcol = sBeta[kSub * R + l16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = kSub * R + 4 * lg + m;
+        sTf[r * LDA + kSub * R + l16] = D[m];
+        sTb[r * LDC + kSub * R + l16] = from_f32<op_t>(D[m] * bcol);
+      }
     }
     __syncthreads();
-    // 4b: block rows R = 1..3: T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI
-    float* sY = reinterpret_cast<float*>(sTb);  // 16x16 float32 scratch per wave
+    // Block rows R = 1..3: T_RI = -D_R sum_{J=I}^{R-1} A_RJ T_JI (wave I), one level per barrier.
 #pragma unroll
     for (int R = 1; R < kNSub; ++R) {
       if (wave < R) {
         const int I = wave;
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        for (int j = kSub * I; j < kSub * R; j += 4) {
-          const float a = sA[(kSub * R + l16) * LDA + j + lg];
-          const float bb = sTf[(j + lg) * LDA + kSub * I + l16];
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, y, 0, 0, 0);
-        }
+        for (int J = I; J < R; ++J) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) sY[wave * 256 + (4 * lg + m) * 16 + l16] = y[m];
-      }
-      __syncthreads();
-      if (wave < R) {
-        const int I = wave;
+          for (int kb = 0; kb < 4; ++kb) {
+            const float a = sA[(kSub * R + l16) * LDA + kSub * J + 4 * lg + kb];
+            const float bb = sTf[(kSub * J + 4 * lg + kb) * LDA + kSub * I + l16];
+            y = mma_f32(a, bb, y);
+          }
+        }
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < kSub; j += 4) {
-          const float a = sTf[(kSub * R + l16) * LDA + kSub * R + j + lg];
-          const float bb = sY[wave * 256 + (j + lg) * 16 + l16];
-          t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, t, 0, 0, 0);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+          t = mma_f32(sTf[(kSub * R + l16) * LDA + kSub * R + 4 * lg + kb], y[kb], t);
+        const float bcol = sBeta[kSub * I + l16];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          sTf[(kSub * R + 4 * lg + m) * LDA + kSub * I + l16] = -t[m];
+        for (int m = 0; m < 4; ++m) {
+          const int r = kSub * R + 4 * lg + m;
+          sTf[r * LDA + kSub * I + l16] = -t[m];
+          sTb[r * LDC + kSub * I + l16] = from_f32<op_t>(-t[m] * bcol);
+        }
       }
       __syncthreads();
     }
-    // 4c: T' = T Diag(beta) as an MFMA operand
-    for (int e = tid; e < kC * kC; e += NT) {
-      const int r = e / kC, j = e % kC;
-      sTb[r * LDC + j] = from_f32<op_t>(sTf[r * LDA + j] * sBeta[j]);
-    }
-    __syncthreads();
 
-    // ---- step 5: W = T' Kc  (-> shared, A's slot), U0 = T' V (-> registers)
-    for (int tt = wave; tt < 4 * (DK / 16); tt += NW) {
-      const int rt = tt / (DK / 16), ct = tt % (DK / 16);
+    // ---- per row tile: W = T' Kc (-> A's slot), U0 = T' V, U = U0 - W S, Qc S.
+    // Both waves of a row tile compute the whole W row tile (they need all of it
+    // as an operand) and store the same values.
+    constexpr int NKT = kC / KS;  // k-steps over the chunk's tokens
+    const int kend = 16 * rt + 16;  // T' and P rows of this tile vanish beyond kend
+    frag aT[NKT];
+#pragma unroll
+    for (int q = 0; q < NKT; ++q)
+      if (q * KS < kend) aT[q] = M::ld(sTb + (16 * rt + l16) * LDC + q * KS + kofs);
+#pragma unroll
+    for (int ct = 0; ct < DK / 16; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < kC; kk += KS) {
-        acc = M::mma(M::ld(sTb + (16 * rt + l16) * LDC + kk + kofs),
-                     M::ld(sKcT + (16 * ct + l16) * LDC + kk + kofs), acc);
-      }
+      for (int q = 0; q < NKT; ++q)
+        if (q * KS < kend) acc = M::mma(aT[q], M::ld(sKcT + (16 * ct + l16) * LDC + q * KS + kofs), acc);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         sW[(16 * rt + 4 * lg + m) * LDK + 16 * ct + l16] = from_f32<op_t>(acc[m]);
     }
-    f32x4 Uacc[NUW];
+    f32x4 Oacc[NJW];
 #pragma unroll
-    for (int i = 0; i < NUW; ++i) {
-      const int tt = wave + NW * i;
-      Uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (tt < NU) {
-        const int rt = tt / (DVS / 16), jt = tt % (DVS / 16);
+    for (int j = 0; j < NJW; ++j) {
+      const int jt = jt0 + j;
+      f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, ws = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < kC; kk += KS) {
-          Uacc[i] = M::mma(M::ld(sTb + (16 * rt + l16) * LDC + kk + kofs),
-                           M::ld(sVT + (16 * jt + l16) * LDC + kk + kofs), Uacc[i]);
-        }
+      for (int q = 0; q < NKT; ++q)
+        if (q * KS < kend) u0 = M::mma(aT[q], M::ld(sVT + (16 * jt + l16) * LDC + q * KS + kofs), u0);
+#pragma unroll 4
+      for (int kk = 0; kk < DK; kk += KS) {
+        const frag bS = M::ld(sST + (16 * jt + l16) * LDK + kk + kofs);
+        ws = M::mma(M::ld(sW + (16 * rt + l16) * LDK + kk + kofs), bS, ws);
+        oq = M::mma(M::ld(sQc + (16 * rt + l16) * LDK + kk + kofs), bS, oq);
+      }
+      Oacc[j] = oq;
+      const int jv = 16 * jt + l16, i0 = 16 * rt + 4 * lg;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float u = u0[m] - ws[m];
+        const op_t uh = from_f32<op_t>(u);
+        sUT[jv * LDC + i0 + m] = uh;
+        if constexpr (BF16) sUT2[jv * LDC + i0 + m] = from_f32<op_t>(u - to_f32(uh));
       }
     }
     __syncthreads();
 
-    // ---- step 6: U = U0 - W S  -> U^T (hi/lo) in shared
+    // ---- O += P U (lower-triangular P), output; S <- Diag(2^G_end) S + Kbar^T U
+    {
+      frag ph[NKT], pl[NKT];
 #pragma unroll
-    for (int i = 0; i < NUW; ++i) {
-      const int tt = wave + NW * i;
-      if (tt < NU) {
-        const int rt = tt / (DVS / 16), jt = tt % (DVS / 16);
-        f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int kk = 0; kk < DK; kk += KS) {
-          ws = M::mma(M::ld(sW + (16 * rt + l16) * LDK + kk + kofs),
-                      M::ld(sST + (16 * jt + l16) * LDK + kk + kofs), ws);
-        }
-        const int jv = 16 * jt + l16, i0 = 16 * rt + 4 * lg;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float u = Uacc[i][m] - ws[m];
-          const op_t uh = from_f32<op_t>(u);
-          sUT[jv * LDC + i0 + m] = uh;
-          if constexpr (BF16) sUT2[jv * LDC + i0 + m] = from_f32<op_t>(u - to_f32(uh));
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- step 7: O = Qc S + P U
-#pragma unroll
-    for (int i = 0; i < NUW; ++i) {
-      const int tt = wave + NW * i;
-      if (tt < NU) {
-        const int rt = tt / (DVS / 16), jt = tt % (DVS / 16);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int kk = 0; kk < DK; kk += KS) {
-          acc = M::mma(M::ld(sQc + (16 * rt + l16) * LDK + kk + kofs),
-                       M::ld(sST + (16 * jt + l16) * LDK + kk + kofs), acc);
-        }
-        const int kend = 16 * rt + 16;  // P is lower triangular
-        for (int kk = 0; kk < kend; kk += KS) {
-          const int k0 = kk + kofs;
+      for (int q = 0; q < NKT; ++q) {
+        if (q * KS < kend) {
+          const int k0 = q * KS + kofs;
           if constexpr (BF16) {
             float pf[8];
             load8(sP + (16 * rt + l16) * LDA + k0, pf);
-            frag ph, pl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const __bf16 hh = (__bf16)pf[e];
-              ph[e] = hh;
-              pl[e] = (__bf16)(pf[e] - (float)hh);
+              const __bf16 hh_ = (__bf16)pf[e];
+              ph[q][e] = hh_;
+              pl[q][e] = (__bf16)(pf[e] - (float)hh_);
             }
-            const frag uh = M::ld(sUT + (16 * jt + l16) * LDC + k0);
-            const frag ul = M::ld(sUT2 + (16 * jt + l16) * LDC + k0);
-            acc = M::mma(ph, uh, acc);
-            acc = M::mma(pl, uh, acc);
-            acc = M::mma(ph, ul, acc);
           } else {
-            acc = M::mma(sP[(16 * rt + l16) * LDA + k0], sUT[(16 * jt + l16) * LDC + k0], acc);
+            ph[q] = sP[(16 * rt + l16) * LDA + k0];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) {
+        const int jt = jt0 + j;
+        f32x4 acc = Oacc[j];
+#pragma unroll
+        for (int q = 0; q < NKT; ++q) {
+          if (q * KS < kend) {
+            const int k0 = q * KS + kofs;
+            const frag uh = M::ld(sUT + (16 * jt + l16) * LDC + k0);
+            acc = M::mma(ph[q], uh, acc);
+            if constexpr (BF16) {
+              const frag ul = M::ld(sUT2 + (16 * jt + l16) * LDC + k0);
+              acc = M::mma(pl[q], uh, acc);
+              acc = M::mma(ph[q], ul, acc);
+            }
           }
         }
 #pragma unroll
@@ -551,19 +584,25 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
         }
       }
     }
-
-    // ---- step 8: S <- Diag(2^G_end) S + Kbar^T U
+    {
+      static_assert(NJT % SPW == 0, "a wave's state tiles share one key-channel tile");
+      const int ct = (SPW * wave) / NJT;
+      frag ak[NKT];
 #pragma unroll
-    for (int i = 0; i < NSW; ++i) {
-      const int tt = wave + NW * i;
-      const int ct = tt / (DVS / 16), jt = tt % (DVS / 16);
+      for (int q = 0; q < NKT; ++q) ak[q] = M::ld(sKbT + (16 * ct + l16) * LDC + q * KS + kofs);
+      f32x4 gam;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) Sacc[i][m] *= sEGam[16 * ct + 4 * lg + m];
+      for (int m = 0; m < 4; ++m) gam[m] = sEGam[16 * ct + 4 * lg + m];
 #pragma unroll
-      for (int kk = 0; kk < kC; kk += KS) {
-        const frag a = M::ld(sKbT + (16 * ct + l16) * LDC + kk + kofs);
-        Sacc[i] = M::mma(a, M::ld(sUT + (16 * jt + l16) * LDC + kk + kofs), Sacc[i]);
-        if constexpr (BF16) Sacc[i] = M::mma(a, M::ld(sUT2 + (16 * jt + l16) * LDC + kk + kofs), Sacc[i]);
+      for (int i = 0; i < SPW; ++i) {
+        const int jt = (SPW * wave + i) % NJT;
+        f32x4 s = Sacc[i] * gam;
+#pragma unroll
+        for (int q = 0; q < NKT; ++q) {
+          s = M::mma(ak[q], M::ld(sUT + (16 * jt + l16) * LDC + q * KS + kofs), s);
+          if constexpr (BF16) s = M::mma(ak[q], M::ld(sUT2 + (16 * jt + l16) * LDC + q * KS + kofs), s);
+        }
+        Sacc[i] = s;
       }
     }
     __syncthreads();
@@ -573,9 +612,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
       const int64_t nck = T / p.ck_every, idx = (n + 1) * kC / p.ck_every - 1;
       float* dst = p.ck + ((b * nck + idx) * H + h) * (int64_t)DK * DV;
 #pragma unroll
-      for (int i = 0; i < NSW; ++i) {
-        const int tt = wave + NW * i;
-        const int ct = tt / (DVS / 16), jt = tt % (DVS / 16);
+      for (int i = 0; i < SPW; ++i) {
+        const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
           dst[(int64_t)(16 * ct + 4 * lg + m) * DV + j0 + 16 * jt + l16] = Sacc[i][m];
@@ -585,9 +623,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
 
   if (p.s_final) {
 #pragma unroll
-    for (int i = 0; i < NSW; ++i) {
-      const int tt = wave + NW * i;
-      const int ct = tt / (DVS / 16), jt = tt % (DVS / 16);
+    for (int i = 0; i < SPW; ++i) {
+      const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         p.s_final[state_off + (int64_t)(16 * ct + 4 * lg + m) * DV + j0 + 16 * jt + l16] =
@@ -596,10 +633,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(PrefillArgs p) {
   }
 }
 
-template <typename TIn, typename TOut, int DK, int DV, int DVS, int NW>
+template <typename TIn, typename TOut, int DK, int DV, int DVS>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   typedef PrefillLayout<TIn, DK, DVS> Lay;
-  auto kern = chunk_fwd_kernel<TIn, TOut, DK, DV, DVS, NW>;
+  auto kern = chunk_fwd_kernel<TIn, TOut, DK, DV, DVS>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      Lay::TOTAL);
   if (e != hipSuccess) return e;
@@ -607,12 +644,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t nheads = a.B * a.H;
   const int64_t groups = (nheads + 7) / 8;
   const int64_t grid = groups * 8 * NSLICE;
-  kern<<<dim3((unsigned)grid), dim3(NW * 64), Lay::TOTAL, stream>>>(a);
+  kern<<<dim3((unsigned)grid), dim3(512), Lay::TOTAL, stream>>>(a);
   return hipGetLastError();
 }
 
 // d_v slice width per workgroup (must match the instantiations in chunk_fwd).
 static int prefill_slice(int dk, int dv, bool in_bf16) {
+  (void)dv;
   if (!in_bf16) return 64;
   return dk == 128 ? 64 : 32;
 }
@@ -625,18 +663,18 @@ hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool ou
                      hipStream_t s) {
   if (in_bf16) {
     if (out_bf16) {
-      if (dk == 128 && dv == 128) return launch_prefill<__bf16, __bf16, 128, 128, 64, 4>(a, s);
-      if (dk == 128 && dv == 64) return launch_prefill<__bf16, __bf16, 128, 64, 64, 4>(a, s);
-      if (dk == 64 && dv == 128) return launch_prefill<__bf16, __bf16, 64, 128, 32, 4>(a, s);
-      return launch_prefill<__bf16, __bf16, 64, 64, 32, 4>(a, s);
+      if (dk == 128 && dv == 128) return launch_prefill<__bf16, __bf16, 128, 128, 64>(a, s);
+      if (dk == 128 && dv == 64) return launch_prefill<__bf16, __bf16, 128, 64, 64>(a, s);
+      if (dk == 64 && dv == 128) return launch_prefill<__bf16, __bf16, 64, 128, 32>(a, s);
+      return launch_prefill<__bf16, __bf16, 64, 64, 32>(a, s);
     }
-    if (dk == 128 && dv == 128) return launch_prefill<__bf16, float, 128, 128, 64, 4>(a, s);
-    if (dk == 128 && dv == 64) return launch_prefill<__bf16, float, 128, 64, 64, 4>(a, s);
-    if (dk == 64 && dv == 128) return launch_prefill<__bf16, float, 64, 128, 32, 4>(a, s);
-    return launch_prefill<__bf16, float, 64, 64, 32, 4>(a, s);
+    if (dk == 128 && dv == 128) return launch_prefill<__bf16, float, 128, 128, 64>(a, s);
+    if (dk == 128 && dv == 64) return launch_prefill<__bf16, float, 128, 64, 64>(a, s);
+    if (dk == 64 && dv == 128) return launch_prefill<__bf16, float, 64, 128, 32>(a, s);
+    return launch_prefill<__bf16, float, 64, 64, 32>(a, s);
   }
-  if (out_bf16) return launch_prefill<float, __bf16, 64, 64, 64, 4>(a, s);
-  return launch_prefill<float, float, 64, 64, 64, 4>(a, s);
+  if (out_bf16) return launch_prefill<float, __bf16, 64, 64, 64>(a, s);
+  return launch_prefill<float, float, 64, 64, 64>(a, s);
 }
 
 }  // namespace kda

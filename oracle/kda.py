@@ -64,10 +64,15 @@ def kda_forward(q, k, v, g, beta, s0=None, checkpoint_every: int = 0):
     return o, S, ck
 
 
-def _one_head(args):
-    q, k, v, g, beta, s0, every = args
-    o, S, ck = kda_forward(q[None, :, None], k[None, :, None], v[None, :, None],
-                           g[None, :, None], beta[None, :, None], s0[None, None], every)
+_SHARED = None  # inputs handed to forked workers without pickling
+
+
+def _one_head(idx):
+    q, k, v, g, beta, s0, every = _SHARED
+    b, h = divmod(idx, q.shape[2])
+    o, S, ck = kda_forward(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h:h + 1],
+                           v[b:b + 1, :, h:h + 1], g[b:b + 1, :, h:h + 1],
+                           beta[b:b + 1, :, h:h + 1], s0[b:b + 1, h:h + 1], every)
     return o[0, :, 0], S[0, 0], None if ck is None else ck[0, :, 0]
 
 
@@ -78,23 +83,27 @@ def kda_forward_heads_parallel(q, k, v, g, beta, s0=None, checkpoint_every: int 
     Identical arithmetic per head; only the scheduling differs.  Returns the
     same triple as :func:`kda_forward` and the number of processes used.
     """
+    global _SHARED
     q, k, v, g, beta = (np.asarray(x, np.float64) for x in (q, k, v, g, beta))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if s0 is None:
         s0 = np.zeros((B, H, dk, dv))
-    jobs = [(q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h], beta[b, :, h], s0[b, h],
-             checkpoint_every) for b in range(B) for h in range(H)]
+    n_jobs = B * H
     if processes is None:
-        processes = len(os.sched_getaffinity(0))
-    processes = max(1, min(processes, len(jobs)))
-    if processes == 1:
-        res = [_one_head(j) for j in jobs]
-    else:
-        import multiprocessing as mp
+        processes = min(16, len(os.sched_getaffinity(0)))
+    processes = max(1, min(processes, n_jobs))
+    _SHARED = (q, k, v, g, beta, np.asarray(s0, np.float64), checkpoint_every)
+    try:
+        if processes == 1:
+            res = [_one_head(i) for i in range(n_jobs)]
+        else:
+            import multiprocessing as mp
 
-        with mp.get_context("fork").Pool(processes) as pool:
-            res = pool.map(_one_head, jobs, chunksize=1)
+            with mp.get_context("fork").Pool(processes) as pool:
+                res = pool.map(_one_head, range(n_jobs), chunksize=1)
+    finally:
+        _SHARED = None
     o = np.empty((B, T, H, dv))
     S = np.empty((B, H, dk, dv))
     ck = np.empty((B, T // checkpoint_every, H, dk, dv)) if checkpoint_every else None

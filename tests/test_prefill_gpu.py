@@ -70,3 +70,38 @@ def test_checkpoints_match_oracle():
 def test_tiny_t_below_one_chunk():
     _check(synth.PREFILL_B4_T4096.replace(B=1, T=1, H=2))
     _check(synth.TINY_F32.replace(T=17))
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+
+def test_prefill_workload_full_size():
+    """4 x 4096 tokens, 32 heads, d = 128, bfloat16: every output and final state."""
+    _check(synth.PREFILL_B4_T4096)
+
+
+def test_decay_floor_workload_full_size():
+    """65,536 tokens x 32 heads with decay logits ~ N(5, 1): most channels sit on the floor."""
+    _check(synth.DECAY_FLOOR_T65536)
+
+
+def test_million_token_prefix_checkpoint():
+    """1,048,576 tokens x 16 heads (inputs drawn on the device); the state after token
+    65,536 (a checkpoint) and o over that prefix against the oracle run on the prefix."""
+    w = synth.MILLION_TOKEN
+    d = synth.device_prefill_inputs(w, DEV)
+    P = 65536
+    o, sf, ck = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"],
+                                  checkpoint_every=P)
+    torch.cuda.synchronize()
+    assert ck.shape[1] == w.T // P
+    x = {n: d[n][:, :P].double().cpu().numpy() for n in ("q", "k", "v", "g", "beta")}
+    s0 = d["s0"].double().cpu().numpy()
+    o_r, s_r, _ = _ref(dict(x, s0=s0))
+    e_o = oracle.rel_l2(o[:, :P].double().cpu().numpy(), o_r)
+    e_s = oracle.rel_l2(ck[:, 0].double().cpu().numpy(), s_r)
+    print(f"[prefill] 1M tokens, prefix {P}: o {e_o:.3e} checkpoint {e_s:.3e}", flush=True)
+    assert e_o <= 3e-3 and e_s <= 3e-3
+    assert bool(torch.isfinite(sf).all()) and bool(torch.isfinite(o.float()).all())
+    # the last checkpoint is the final state
+    assert torch.equal(ck[:, -1], sf)
