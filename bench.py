@@ -8,6 +8,7 @@ The same run also times kda_recurrent_step on the 256-sequence decode workload
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +36,50 @@ def prefill_bytes(B, T, H, dk, dv, in_bytes=2, out_bytes=2) -> float:
 def decode_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2) -> float:
     per_head = 2 * dk * dv * 4 + (3 * dk + dv + 1) * in_bytes + dv * out_bytes
     return N * H * per_head
+
+
+KERNEL_SOURCES = {
+    "prefill": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_prefill.hip"),
+    "decode": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COPY_CALIBRATION_BYTES = 1 << 30
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(which: str):
+    """HBM bytes per launch from the committed counter summary, or None when that
+    summary was taken on a different version of the kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[which]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[which]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(torch, reps: int = 3):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    n = COPY_CALIBRATION_BYTES // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    print(json.dumps({"copy_calibration": {"bytes_read": COPY_CALIBRATION_BYTES,
+                                           "bytes_written": COPY_CALIBRATION_BYTES,
+                                           "ms": ms,
+                                           "GBps": 2 * COPY_CALIBRATION_BYTES / ms / 1e6}}))
 
 
 def time_prefill(kda, torch, w, steps, warmup):
@@ -115,6 +160,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-sample-heads", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the KDA path here has "
@@ -122,6 +169,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import gated_delta_rule_57_amd as kda
     import synth
@@ -150,8 +201,8 @@ def main():
                    "chunk": w.chunk, "inputs": "bf16", "state": "f32", "output": "bf16",
                    "decay_logits": "N(0,2)"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "chunk_fwd_kernel<bf16,bf16,128,128,64,4>",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("prefill"),
+                     "kernel": "chunk_fwd_kernel<bf16,bf16,128,128,64>",
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
@@ -164,7 +215,7 @@ def main():
         line["decode"] = {"workload": wd.name, "us_per_step": us, "steps_timed": args.decode_steps,
                           "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                                        "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                                       "traffic": None,
+                                       "traffic": measured_traffic("decode"),
                                        "kernel": "decode_step_kernel<bf16,bf16,128,128>",
                                        "algorithmic_bytes_per_launch": db}}
     if not args.no_cpu_baseline:

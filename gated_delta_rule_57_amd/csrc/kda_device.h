@@ -63,6 +63,41 @@ __device__ __forceinline__ void store8(float* p, const float* x) {
   *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// Unpack 16 raw bytes held in a float4 register into floats (8 bfloat16 or 4
+// float32 values) with bit operations only, so the register never goes to memory.
+__device__ __forceinline__ void unpack16(const float4& raw, __bf16*, float* out) {
+  const uint32_t w[4] = {__float_as_uint(raw.x), __float_as_uint(raw.y), __float_as_uint(raw.z),
+                         __float_as_uint(raw.w)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const float4& raw, float*, float* out) {
+  out[0] = raw.x;
+  out[1] = raw.y;
+  out[2] = raw.z;
+  out[3] = raw.w;
+}
+
+__device__ __forceinline__ uint4 mask4(const float4& x, uint32_t m) {
+  return make_uint4(__float_as_uint(x.x) & m, __float_as_uint(x.y) & m, __float_as_uint(x.z) & m,
+                    __float_as_uint(x.w) & m);
+}
+
+// Access at a uniform base plus a 32-bit byte offset: this form lets the backend
+// use the scalar-base addressing mode (SGPR base + one VGPR offset) instead of
+// a 64-bit address per lane.
+template <typename T>
+__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void st_at(void* base, uint32_t byte_off, T x) {
+  *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off) = x;
+}
+
 // Wave-wide sum (64 lanes).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -37,6 +37,8 @@
 //   diagonal 16x16 inverses, (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8) on MFMA
 //   from registers | three block-substitution levels | per row tile: W, U0,
 //   U = U0 - W S, Qc S | P U, output, state update | state to its MFMA operand.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -148,9 +150,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   constexpr int SPT = RPC / kSub;        // sub-tiles per channel-major thread
   constexpr int E16 = 16 / sizeof(TIn);  // input elements per 16-byte load
   constexpr int NPF = kC * DK / E16 / NT;
-  constexpr int NVP = kC * DVS / E16;    // 16-byte pieces of v per chunk
-  constexpr int NPV = (NVP + NT - 1) / NT;
-  static_assert(NPF * E16 * NT == kC * DK, "load layout");
+  constexpr int NVT = DVS * (kC / 8);    // v loaders: one value column x 8 tokens each
+  static_assert(NPF * E16 * NT == kC * DK && NVT <= NT, "load layout");
   static_assert(SPW * NW == NST && NJW >= 1 && SPT >= 1 && NCM <= NT, "layout");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -176,13 +177,20 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   float* sPair = sm + Lay::SM_PAIR;
   float* sEGam = sm + Lay::SM_EGAM;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l16 = lane & 15;
-  const int lg = lane >> 4;
-  const int kofs = lg * KPL;
-  const int rt = wave & 3;       // row tile of the chunk owned by this wave
+  // Lane indices are refreshed at the top of every chunk (see refresh_lane):
+  // the many per-lane shared-memory addresses derived from them are then cheap
+  // to recompute inside the loop instead of occupying registers across it.
+  int tid = threadIdx.x, lane, l16, lg, kofs;
+  auto refresh_lane = [&]() {
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    l16 = lane & 15;
+    lg = lane >> 4;
+    kofs = lg * KPL;
+  };
+  refresh_lane();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt = wave & 3;            // row tile of the chunk owned by this wave
   const int jt0 = (wave >> 2) * NJW;  // its first value-column tile
 
   // Workgroup -> (head, slice): consecutive workgroups are dealt round-robin to
@@ -228,88 +236,121 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   };
   store_state_operand();
 
-  // ---- register prefetch of one chunk of raw inputs (16-byte pieces)
-  float4 pk[NPF], pq[NPF], pg[NPF], pv[NPV];
-  float pbeta = 0.f;
-  auto prefetch = [&](int64_t t0) {
+  // ---- register prefetch of one chunk of raw inputs (16-byte pieces).  Addresses
+  // are a uniform 64-bit chunk base plus 32-bit per-thread offsets.
+  float4 pk[NPF], pq[NPF], pg[NPF];
+  // 8 consecutive tokens of one value column, raw bits in 32-bit containers (no
+  // packing at load time, which would wait for the loads)
+  typedef typename std::conditional<sizeof(TIn) == 2, uint16_t, uint32_t>::type raw_t;
+  uint32_t pv[8];
+  TIn pbeta = from_f32<TIn>(0.f);  // kept raw: converting here would wait for the load
+  // token strides (elements); offsets inside one chunk fit in 32 bits
+  const uint32_t rs_k = (uint32_t)(H * DK), rs_v = (uint32_t)(H * DV), rs_b = (uint32_t)H;
+  // Rows past the end of the sequence load the last valid token (always in
+  // bounds) and are zeroed when staged, so the loads themselves are branch-free.
+  // The loads are issued in four parts spread over the chunk's phases, so that
+  // the memory pipeline is not asked for a whole chunk at once.
+  auto prefetch = [&](int64_t t0, int part) {
+    const int64_t cb = (b * T + t0) * H + h;
+    const int last = (int)((T - t0) < kC ? (T - t0) : kC) - 1;
+    if (part == 0) {
+      const TIn* vb = gv + cb * DV + j0;
+      if (tid < NVT) {
+        const int jv = tid % DVS, r0v = 8 * (tid / DVS);
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      const int pc = tid + NT * i;
-      const int r = pc / (DK / E16), c = (pc % (DK / E16)) * E16;
-      const int64_t t = t0 + r;
-      if (t < T) {
-        const int64_t off = ((b * T + t) * H + h) * DK + c;
-        pk[i] = *reinterpret_cast<const float4*>(gk + off);
-        pq[i] = *reinterpret_cast<const float4*>(gq + off);
-        pg[i] = *reinterpret_cast<const float4*>(gg + off);
-      } else {
-        pk[i] = pq[i] = pg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < 8; ++e) {
+          const int r = r0v + e < last ? r0v + e : last;
+          pv[e] = ld_at<raw_t>(vb, ((uint32_t)r * rs_v + (uint32_t)jv) * (uint32_t)sizeof(TIn));
+        }
       }
+      return;
     }
+    const TIn* base = (part == 1 ? gk : part == 2 ? gq : gg) + cb * DK;
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
+    for (int i = 0; i < NPF; ++i) {
       const int pc = tid + NT * i;
-      const int r = pc / (DVS / E16), jv = (pc % (DVS / E16)) * E16;
-      const int64_t t = t0 + r;
-      pv[i] = (pc < NVP && t < T)
-                  ? *reinterpret_cast<const float4*>(gv + ((b * T + t) * H + h) * DV + j0 + jv)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int r = min(pc / (DK / E16), last), c = (pc % (DK / E16)) * E16;
+      const float4 x = ld_at<float4>(base, ((uint32_t)r * rs_k + (uint32_t)c) * (uint32_t)sizeof(TIn));
+      if (part == 1) pk[i] = x;
+      else if (part == 2) pq[i] = x;
+      else pg[i] = x;
     }
-    if (tid < kC) pbeta = (t0 + tid < T) ? to_f32(gb[(b * T + t0 + tid) * H + h]) : 0.f;
+    if (part == 3 && tid < kC)
+      pbeta = ld_at<TIn>(gb + cb, (uint32_t)min(tid, last) * rs_b * (uint32_t)sizeof(TIn));
   };
-
-  const int64_t nchunks = (T + kC - 1) / kC;
-  prefetch(0);
-
-  for (int64_t n = 0; n < nchunks; ++n) {
-    const int64_t t0 = n * kC;
-    // ---- stage the prefetched chunk: k, q raw; g -> gamma (float32); v^T; beta
+  // Prefetched chunk starting at token t0 -> shared memory: k, q raw; g -> gamma
+  // (float32); v^T; beta.  Rows past the end become beta = 0, g = 0, k = q = v = 0
+  // tokens, which leave the state unchanged.
+  auto stage = [&](int64_t t0) {
+    const int nvalid = (int)((T - t0) < kC ? (T - t0) : kC);
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
       const int pc = tid + NT * i;
       const int r = pc / (DK / E16), c = (pc % (DK / E16)) * E16;
-      *reinterpret_cast<float4*>(sK + r * LDK + c) = pk[i];
-      *reinterpret_cast<float4*>(sQ + r * LDK + c) = pq[i];
+      // bitwise masks (a select between registers here becomes a select between
+      // addresses, which sends the prefetch registers to scratch memory)
+      const uint32_t mk = r < nvalid ? 0xffffffffu : 0u;
+      *reinterpret_cast<uint4*>(sK + r * LDK + c) = mask4(pk[i], mk);
+      *reinterpret_cast<uint4*>(sQ + r * LDK + c) = mask4(pq[i], mk);
       float gf[E16];
-      load16(reinterpret_cast<const TIn*>(&pg[i]), gf);
+      unpack16(pg[i], (TIn*)nullptr, gf);
 #pragma unroll
-      for (int e = 0; e < E16; ++e) gf[e] = clamp_log_decay(gf[e]) * kLog2e;
+      for (int e = 0; e < E16; ++e)
+        gf[e] = __uint_as_float(__float_as_uint(clamp_log_decay(gf[e]) * kLog2e) & mk);
       if constexpr (E16 == 8) {
         store8(sL + r * LDF + c, gf);
       } else {
         *reinterpret_cast<f32x4*>(sL + r * LDF + c) = f32x4{gf[0], gf[1], gf[2], gf[3]};
       }
     }
+    if (tid < NVT) {
+      const int jv = tid % DVS, r0v = 8 * (tid / DVS);
+      uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
-      const int pc = tid + NT * i;
-      if (pc >= NVP) break;
-      const int r = pc / (DVS / E16), jv = (pc % (DVS / E16)) * E16;
-      float vf[E16];
-      load16(reinterpret_cast<const TIn*>(&pv[i]), vf);
-#pragma unroll
-      for (int e = 0; e < E16; ++e) sVT[(jv + e) * LDC + r] = from_f32<op_t>(vf[e]);
+      for (int e = 0; e < 8; ++e) w[e] = (r0v + e < nvalid) ? pv[e] : 0u;
+      op_t* dst = sVT + jv * LDC + r0v;
+      if constexpr (BF16) {
+        *reinterpret_cast<uint4*>(dst) =
+            make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
+      } else {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(dst + 4) = make_uint4(w[4], w[5], w[6], w[7]);
+      }
     }
-    if (tid < kC) sBeta[tid] = pbeta;
-    if (n + 1 < nchunks) prefetch(t0 + kC);
-    __syncthreads();
+    if (tid < kC) sBeta[tid] = (tid < nvalid) ? to_f32(pbeta) : 0.f;
+  };
 
+  const int64_t nchunks = (T + kC - 1) / kC;
+  for (int part = 0; part < 4; ++part) prefetch(0, part);
+  stage(0);
+  __syncthreads();
+
+  for (int64_t n = 0; n < nchunks; ++n) {
+    const int64_t t0 = n * kC;
+    refresh_lane();
+    // Next chunk's inputs: loaded while this chunk computes, staged at its end.  The
+    // last chunk reloads itself (in bounds, never used) so that loads and staging
+    // are unconditional.
+    const int64_t tn = (n + 1 < nchunks) ? t0 + kC : t0;
+    prefetch(tn, 0);
     // ---- sub-tile cumulative log-decay: one thread per (channel, token range)
     const int cc = tid % DK, hh = tid / DK, r0 = RPC * hh;
     const bool cm = tid < NCM;  // this thread takes part in the channel-major phases
-    float Lr[RPC];
+    float Lr[RPC];  // gamma of each token of this thread
 #pragma unroll
     for (int s = 0; s < SPT && cm; ++s) {
       float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < kSub; ++j) {
-        acc += sL[(r0 + kSub * s + j) * LDF + cc];
-        Lr[kSub * s + j] = acc;
+        const float gm = sL[(r0 + kSub * s + j) * LDF + cc];
+        acc += gm;
+        Lr[kSub * s + j] = gm;
       }
       sTau[(r0 / kSub + s) * DK + cc] = acc;
     }
     __syncthreads();
 
+    prefetch(tn, 1);
     // ---- operands (same thread, same elements, so the updates are in place)
     typedef op_t vec8 __attribute__((ext_vector_type(8)));
     vec8 dKc[RPC / 8], dQc[RPC / 8], dKb[RPC / 8];
@@ -336,11 +377,30 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
           if (J >= R) suf += tau[J];
         }
         const float eref = exp2_hw(ref), ebar = exp2_hw(suf);
+        // 2^L_j (L = inclusive sub-tile sum) and 2^-L_j as prefix / suffix products of
+        // 2^gamma: one exp2 per token instead of two.
+        float ep_[kSub], em_[kSub];
+        {
+          float f[kSub];
+#pragma unroll
+          for (int j = 0; j < kSub; ++j) f[j] = exp2_hw(Lr[kSub * s + j]);
+          float pre = 1.f, suf_p = exp2_hw(-tau[R]);
+#pragma unroll
+          for (int j = 0; j < kSub; ++j) {
+            pre *= f[j];
+            ep_[j] = pre;
+          }
+#pragma unroll
+          for (int j = kSub - 1; j >= 0; --j) {
+            em_[j] = suf_p;
+            suf_p *= f[j];
+          }
+        }
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
           const int r = r0 + kSub * s + j, e = kSub * s + j;
           const float kf = to_f32(sK[r * LDK + cc]), qf = to_f32(sQ[r * LDK + cc]);
-          const float ep = exp2_hw(Lr[e]), em = exp2_hw(-Lr[e]);
+          const float ep = ep_[j], em = em_[j];
           const float kr = kf * ep, qr = qf * ep, kd = kf * em;
           sK[r * LDK + cc] = from_f32<op_t>(kr);
           const op_t qh = from_f32<op_t>(qr);
@@ -355,6 +415,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
+    prefetch(tn, 2);
     // ---- A and P tiles, every tile pair one dense product
     for (int pi = wave; pi < 10; pi += NW) {
       // pair order (R, I): (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
@@ -414,6 +475,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
+    prefetch(tn, 3);
     // ---- deferred operands into the released region (channel-major threads):
     // k 2^G and k 2^(G_end - G) transposed (token-contiguous), q 2^G row-major.
 #pragma unroll
@@ -465,34 +527,55 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       }
     }
     __syncthreads();
-    // Block rows R = 1..3: T_RI = -D_R sum_{J=I}^{R-1} A_RJ T_JI (wave I), one level per barrier.
-#pragma unroll
-    for (int R = 1; R < kNSub; ++R) {
-      if (wave < R) {
-        const int I = wave;
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        for (int J = I; J < R; ++J) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const float a = sA[(kSub * R + l16) * LDA + kSub * J + 4 * lg + kb];
-            const float bb = sTf[(kSub * J + 4 * lg + kb) * LDA + kSub * I + l16];
-            y = mma_f32(a, bb, y);
-          }
-        }
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    // Off-diagonal blocks, all six at once (wave w < 6 takes one):
+    //   T_RI = -D_R sum_{J=I}^{R-1} A_RJ T_JI,
+    // each wave recomputing in registers the lower blocks T_JI its block needs.
+    // Products Z = X Y take X from shared memory (read transposed, as the MFMA
+    // A operand) and Y either from shared memory or from registers (result layout).
+    if (wave < 6) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      auto mul_lr = [&](const float* X, int rx, int cx, const f32x4& Y, f32x4 acc) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          t = mma_f32(sTf[(kSub * R + l16) * LDA + kSub * R + 4 * lg + kb], y[kb], t);
-        const float bcol = sBeta[kSub * I + l16];
+          acc = mma_f32(X[(rx + l16) * LDA + cx + 4 * lg + kb], Y[kb], acc);
+        return acc;
+      };
+      auto mul_ll = [&](const float* X, int rx, int cx, const float* Y, int ry, int cy, f32x4 acc) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = kSub * R + 4 * lg + m;
-          sTf[r * LDA + kSub * I + l16] = -t[m];
-          sTb[r * LDC + kSub * I + l16] = from_f32<op_t>(-t[m] * bcol);
-        }
+        for (int kb = 0; kb < 4; ++kb)
+          acc = mma_f32(X[(rx + l16) * LDA + cx + 4 * lg + kb], Y[(ry + 4 * lg + kb) * LDA + cy + l16], acc);
+        return acc;
+      };
+      // A_RI D_I (the diagonal blocks D_I are in sTf)
+      auto a_d = [&](int R, int I, f32x4 acc) { return mul_ll(sA, kSub * R, kSub * I, sTf, kSub * I, kSub * I, acc); };
+      // -D_R Y
+      auto neg_d = [&](int R, const f32x4& Y) { return -mul_lr(sTf, kSub * R, kSub * R, Y, z); };
+      // A_RJ Y
+      auto a_r = [&](int R, int J, const f32x4& Y, f32x4 acc) { return mul_lr(sA, kSub * R, kSub * J, Y, acc); };
+      int R, I;
+      f32x4 t;
+      if (wave < 3) {  // (1,0) (2,1) (3,2)
+        I = wave;
+        R = wave + 1;
+        t = neg_d(R, a_d(R, I, z));
+      } else if (wave < 5) {  // (2,0) (3,1)
+        I = wave - 3;
+        R = wave - 1;
+        const f32x4 tl = neg_d(I + 1, a_d(I + 1, I, z));  // T_{I+1,I}
+        t = neg_d(R, a_r(R, I + 1, tl, a_d(R, I, z)));
+      } else {  // (3,0)
+        I = 0;
+        R = 3;
+        const f32x4 t10 = neg_d(1, a_d(1, 0, z));
+        const f32x4 t20 = neg_d(2, a_r(2, 1, t10, a_d(2, 0, z)));
+        t = neg_d(3, a_r(3, 2, t20, a_r(3, 1, t10, a_d(3, 0, z))));
       }
-      __syncthreads();
+      const float bcol = sBeta[kSub * I + l16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        sTb[(kSub * R + 4 * lg + m) * LDC + kSub * I + l16] = from_f32<op_t>(t[m] * bcol);
     }
+    __syncthreads();
 
     // ---- per row tile: W = T' Kc (-> A's slot), U0 = T' V, U = U0 - W S, Qc S.
     // Both waves of a row tile compute the whole W row tile (they need all of it
@@ -503,7 +586,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
     for (int q = 0; q < NKT; ++q)
       if (q * KS < kend) aT[q] = M::ld(sTb + (16 * rt + l16) * LDC + q * KS + kofs);
-#pragma unroll
+#pragma unroll 2
     for (int ct = 0; ct < DK / 16; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -514,6 +597,9 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         sW[(16 * rt + 4 * lg + m) * LDK + 16 * ct + l16] = from_f32<op_t>(acc[m]);
     }
     f32x4 Oacc[NJW];
+    TOut* sO = reinterpret_cast<TOut*>(smem + Lay::O_A);  // [64][LDO] output staging
+    constexpr int LDO = DVS + 16 / (int)sizeof(TOut);
+    static_assert(kC * (DVS + 16 / (int)sizeof(TOut)) * (int)sizeof(TOut) <= Lay::SZ_AW, "O staging");
 #pragma unroll
     for (int j = 0; j < NJW; ++j) {
       const int jt = jt0 + j;
@@ -521,7 +607,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
       for (int q = 0; q < NKT; ++q)
         if (q * KS < kend) u0 = M::mma(aT[q], M::ld(sVT + (16 * jt + l16) * LDC + q * KS + kofs), u0);
-#pragma unroll 4
+#pragma unroll 2
       for (int kk = 0; kk < DK; kk += KS) {
         const frag bS = M::ld(sST + (16 * jt + l16) * LDK + kk + kofs);
         ws = M::mma(M::ld(sW + (16 * rt + l16) * LDK + kk + kofs), bS, ws);
@@ -577,11 +663,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
             }
           }
         }
+        // O tile -> shared memory (A/W slot, free after the row-tile phase)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int64_t t = t0 + 16 * rt + 4 * lg + m;
-          if (t < T) go[((b * T + t) * H + h) * DV + j0 + 16 * jt + l16] = from_f32<TOut>(acc[m]);
-        }
+        for (int m = 0; m < 4; ++m)
+          sO[(16 * rt + 4 * lg + m) * LDO + 16 * jt + l16] = from_f32<TOut>(acc[m]);
       }
     }
     {
@@ -605,8 +690,21 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         Sacc[i] = s;
       }
     }
+    store_state_operand();  // only the row-tile phase reads it, and that phase is over
     __syncthreads();
-    store_state_operand();
+    stage(tn);
+    {  // output: one 16-byte store per piece, rows of DVS contiguous values
+      constexpr int PPR = DVS * (int)sizeof(TOut) / 16;  // 16-byte pieces per row
+      const int64_t ob = ((b * T + t0) * H + h) * DV + j0;
+      const int nvalid = (int)((T - t0) < kC ? (T - t0) : kC);
+#pragma unroll
+      for (int pc = tid; pc < kC * PPR; pc += NT) {
+        const int r = pc / PPR, c = (pc % PPR) * (16 / (int)sizeof(TOut));
+        if (r < nvalid)
+          st_at<uint4>(go + ob, ((uint32_t)r * rs_v + (uint32_t)c) * (uint32_t)sizeof(TOut),
+                       *reinterpret_cast<const uint4*>(sO + r * LDO + c));
+      }
+    }
 
     if (p.ck && ((n + 1) * kC) % p.ck_every == 0 && (n + 1) * kC <= T) {
       const int64_t nck = T / p.ck_every, idx = (n + 1) * kC / p.ck_every - 1;
@@ -619,6 +717,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
           dst[(int64_t)(16 * ct + 4 * lg + m) * DV + j0 + 16 * jt + l16] = Sacc[i][m];
       }
     }
+    __syncthreads();
   }
 
   if (p.s_final) {
