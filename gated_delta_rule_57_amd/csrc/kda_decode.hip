@@ -106,7 +106,10 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
     x.y += kc * u4.y;
     x.z += kc * u4.z;
     x.w += kc * u4.w;
-    st[c * CG + cg] = x;
+    // The state is not read again by this launch: a streaming store keeps it
+    // from displacing lines that other workgroups are still reading.
+    __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w},
+                                reinterpret_cast<f32x4*>(&st[c * CG + cg]));
   }
 }
 

@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       const float* pair = (I < R) ? sPair + (R * (R - 1) / 2 + I) * DK : nullptr;
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
       const int row = kSub * R + l16, col = kSub * I + l16;
-#pragma unroll 1
+#pragma unroll
       for (int kk = 0; kk < DK; kk += KS) {
         const int k0 = kk + kofs;
         const frag aK = M::ld(sK + row * LDK + k0);
@@ -586,7 +586,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
     for (int q = 0; q < NKT; ++q)
       if (q * KS < kend) aT[q] = M::ld(sTb + (16 * rt + l16) * LDC + q * KS + kofs);
-#pragma unroll 2
+#pragma unroll 4
     for (int ct = 0; ct < DK / 16; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -607,7 +607,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
       for (int q = 0; q < NKT; ++q)
         if (q * KS < kend) u0 = M::mma(aT[q], M::ld(sVT + (16 * jt + l16) * LDC + q * KS + kofs), u0);
-#pragma unroll 2
+#pragma unroll
       for (int kk = 0; kk < DK; kk += KS) {
         const frag bS = M::ld(sST + (16 * jt + l16) * LDK + kk + kofs);
         ws = M::mma(M::ld(sW + (16 * rt + l16) * LDK + kk + kofs), bS, ws);
