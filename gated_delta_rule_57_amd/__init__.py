@@ -1,7 +1,7 @@
 """Kimi Delta Attention (KDA) on AMD MI355X: Python binding of the C-ABI library libkda.so.
 
 The binding only marshals arguments (device pointers, sizes, dtypes, the
-current HIP stream) into the two entry points declared in include/kda.h; every
+current HIP stream) into the entry points declared in include/kda.h; every
 step of the computation runs in the library's gfx950 kernels.  There is no
 fallback: if libkda.so is missing or a GPU is absent, calls raise.
 """
@@ -20,7 +20,8 @@ KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",
           -4: "KDA_ERR_ALIGN", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_ALIAS", -7: "KDA_ERR_HIP"}
 EXPORTS = ("kda_status_str", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-           "kda_recurrent_step")
+           "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_bytes",
+           "kda_chunk_fwd_segment_tokens", "kda_recurrent_step")
 
 _lib = None
 
@@ -47,6 +48,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = c_int
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, c_int,
                                   c_int, c_int, c_int, c_int, vp, sz, vp]
+    lib.kda_chunk_fwd_segmented.restype = c_int
+    lib.kda_chunk_fwd_segmented.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                            c_int, c_int, c_int, c_int, c_int, i64, vp, sz, vp]
+    lib.kda_chunk_fwd_segmented_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_segmented_workspace_bytes.argtypes = [i64, i64, i64, c_int, c_int, c_int,
+                                                            c_int, i64]
+    lib.kda_chunk_fwd_segment_tokens.restype = i64
+    lib.kda_chunk_fwd_segment_tokens.argtypes = [i64, i64, i64, c_int, c_int, c_int, c_int]
     lib.kda_recurrent_step.restype = c_int
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, c_int, c_int, c_int,
                                        c_int, vp]
@@ -88,14 +97,32 @@ def kda_chunk_fwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, chun
                                                             _dtype_code(in_dtype)))
 
 
+def kda_chunk_fwd_segmented_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int,
+                                            segment_tokens: int, chunk: int = 64,
+                                            in_dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(load_library().kda_chunk_fwd_segmented_workspace_bytes(
+        B, T, H, dk, dv, chunk, _dtype_code(in_dtype), segment_tokens))
+
+
+def kda_chunk_fwd_segment_tokens(B: int, T: int, H: int, dk: int, dv: int, chunk: int = 64,
+                                 in_dtype: torch.dtype = torch.bfloat16) -> int:
+    """Segment length kda_chunk_fwd picks for these sizes (>= T: one segment)."""
+    return int(load_library().kda_chunk_fwd_segment_tokens(B, T, H, dk, dv, chunk,
+                                                           _dtype_code(in_dtype)))
+
+
 def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=None,
                   final_state=None, want_final_state=True, checkpoint_every: int = 0,
-                  checkpoints=None, chunk: int = 64, workspace=None, stream=None):
+                  checkpoints=None, chunk: int = 64, workspace=None, stream=None,
+                  segment_tokens: Optional[int] = None):
     """Chunked KDA forward.  Shapes as in include/kda.h; returns (o, final_state, checkpoints).
 
     q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (all one dtype); initial_state
     [B,H,dk,dv] float32 or None.  Outputs are allocated when not given; pass
-    final_state=initial_state for an in-place state update.
+    final_state=initial_state for an in-place state update.  ``segment_tokens``
+    None calls kda_chunk_fwd (the library picks the segmentation); an integer
+    calls kda_chunk_fwd_segmented with that segment length.  A workspace of the
+    size the library asks for is allocated when not given.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -108,17 +135,26 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
     if checkpoint_every and checkpoints is None:
         checkpoints = torch.empty((B, T // checkpoint_every, H, dk, dv), dtype=torch.float32,
                                   device=q.device)
-    ws_bytes = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, in_dt)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if segment_tokens is None:
+        need = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, in_dt)
+    else:
+        need = kda_chunk_fwd_segmented_workspace_bytes(B, T, H, dk, dv, segment_tokens, chunk,
+                                                       in_dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                           _ptr(o), _ptr(final_state), _ptr(checkpoints), int(checkpoint_every),
-                           B, T, H, dk, dv, chunk, _dtype_code(in_dt), _dtype_code(o.dtype),
-                           _ptr(workspace), ws_bytes if workspace is not None else 0,
-                           _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+            _ptr(final_state), _ptr(checkpoints), int(checkpoint_every), B, T, H, dk, dv, chunk,
+            _dtype_code(in_dt), _dtype_code(o.dtype))
+    tail = (_ptr(workspace), ws_bytes, _stream(stream))
+    if segment_tokens is None:
+        st, where = lib.kda_chunk_fwd(*args, *tail), "kda_chunk_fwd"
+    else:
+        st = lib.kda_chunk_fwd_segmented(*args, int(segment_tokens), *tail)
+        where = "kda_chunk_fwd_segmented"
     if st != 0:
-        raise KdaError(st, "kda_chunk_fwd")
+        raise KdaError(st, where)
     return o, final_state, checkpoints
 
 

@@ -49,43 +49,96 @@ extern "C" const char* kda_status_str(kda_status_t s) {
   return "KDA_ERR_UNKNOWN";
 }
 
-extern "C" size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv,
-                                                int chunk, kda_dtype_t in) {
-  (void)B;
-  (void)T;
-  (void)H;
-  (void)dk;
-  (void)dv;
-  (void)chunk;
-  (void)in;
-  return 0;  // the fused kernel keeps every intermediate on chip
+namespace {
+
+constexpr int64_t kChunk = 64;
+// Compute units of an MI355X.  The prefill kernel runs one workgroup per CU
+// (its shared memory and register use admit no second one), so a launch of n
+// workgroups takes ceil(n / kCUs) rounds.
+constexpr int64_t kCUs = 256;
+
+bool sizes_ok(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk, kda_dtype_t in) {
+  if (!dtype_ok(in) || B < 1 || T < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv) ||
+      chunk != kChunk)
+    return false;
+  if (in == KDA_F32 && (dk != 64 || dv != 64)) return false;
+  return mul_ok(B, T) && mul_ok(B * T, H) && mul_ok(B * T * H, 128);
 }
 
-extern "C" kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
-                                      const void* beta, const float* initial_state, void* o,
-                                      float* final_state, float* checkpoints,
-                                      int64_t checkpoint_every, int64_t B, int64_t T, int64_t H,
-                                      int dk, int dv, int chunk, kda_dtype_t in, kda_dtype_t out,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+int64_t num_segments(int64_t T, int64_t seg_len) { return seg_len >= T ? 1 : (T + seg_len - 1) / seg_len; }
+
+// Segment length chosen by kda_chunk_fwd: the one that minimises a round count
+// model of the three launches (summaries, scan, outputs) when that beats one
+// segment by 20% or more; T rounded up to whole chunks (one segment) otherwise.
+// Deterministic in the sizes.
+int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, bool bf16) {
+  const int64_t nch = (T + kChunk - 1) / kChunk;
+  const int sl = kda::prefill_slice(dk, dv, bf16);
+  const int64_t ns = dv / sl, np = dk / sl;
+  auto rounds = [](int64_t wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
+  const double one = rounds(B * H * ns) * (double)nch;
+  double best = one;
+  int64_t best_len = nch * kChunk;  // one segment
+  for (int64_t want = 2; want <= 64 && want <= nch; ++want) {
+    const int64_t segc = (nch + want - 1) / want;  // chunks per segment
+    const int64_t n = (nch + segc - 1) / segc;     // segments that length gives
+    if (n != want) continue;
+    const double summary = rounds(B * H * ((n - 1) * (ns + np) - np)) * (double)segc;
+    const double outputs = rounds(B * n * H * ns) * (double)segc;
+    // a scan step costs about a third of a chunk step; the two extra launches
+    // about a chunk step each
+    const double extra = 0.3 * (double)n + 2.0;
+    const double cost = summary + outputs + extra;
+    if (cost < best) {
+      best = cost;
+      best_len = segc * kChunk;
+    }
+  }
+  return best <= 0.8 * one ? best_len : nch * kChunk;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the segmented path: entry states and end-from-zero states
+// [B, nseg, H, dk, dv], transitions [B, nseg, H, dk, dk], float32.
+size_t segment_workspace(int64_t B, int64_t H, int64_t nseg, int dk, int dv, size_t* off_z,
+                         size_t* off_p) {
+  if (nseg <= 1) return 0;
+  const size_t n_in = align256((size_t)(B * nseg * H) * (size_t)dk * (size_t)dv * 4);
+  const size_t n_p = align256((size_t)(B * nseg * H) * (size_t)dk * (size_t)dk * 4);
+  if (off_z) *off_z = n_in;
+  if (off_p) *off_p = 2 * n_in;
+  return 2 * n_in + n_p;
+}
+
+kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, void* o,
+                            float* final_state, float* checkpoints, int64_t checkpoint_every,
+                            int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+                            kda_dtype_t in, kda_dtype_t out, int64_t seg_len, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
   if (checkpoint_every != 0 && !checkpoints) return KDA_ERR_NULL;
   if (!dtype_ok(in) || !dtype_ok(out)) return KDA_ERR_DTYPE;
-  if (B < 1 || T < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv) || chunk != 64)
-    return KDA_ERR_SHAPE;
-  if (in == KDA_F32 && (dk != 64 || dv != 64)) return KDA_ERR_SHAPE;
+  if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return KDA_ERR_SHAPE;
   if (checkpoint_every < 0 || (checkpoint_every % chunk) != 0) return KDA_ERR_SHAPE;
-  if (!mul_ok(B, T) || !mul_ok(B * T, H) || !mul_ok(B * T * H, 128)) return KDA_ERR_SHAPE;
-  const int64_t heads = B * H;
-  if (kda::prefill_grid(heads, dk, dv, in == KDA_BF16) > INT32_MAX) return KDA_ERR_SHAPE;
+  if (seg_len < 1 || seg_len % chunk != 0) return KDA_ERR_SHAPE;
+  const int64_t nseg = num_segments(T, seg_len);
+  const bool bf16 = in == KDA_BF16;
+  const int sl = kda::prefill_slice(dk, dv, bf16);
+  if (!mul_ok(B * H, nseg) || kda::prefill_grid(B * H * nseg, (dv + dk) / sl) > INT32_MAX)
+    return KDA_ERR_SHAPE;
+  size_t off_z = 0, off_p = 0;
+  const size_t ws_need = segment_workspace(B, H, nseg, dk, dv, &off_z, &off_p);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
-  const void* ptrs[] = {q, k, v, g, beta, initial_state, o, final_state, checkpoints};
+  const void* ptrs[] = {q, k, v, g, beta, initial_state, o, final_state, checkpoints, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
 
   const int64_t es = esize(in);
   const int64_t ntok = B * T * H;
+  const int64_t heads = B * H;
   const Span sq = span(q, ntok * dk * es), sk = span(k, ntok * dk * es);
   const Span sv = span(v, ntok * dv * es), sg = span(g, ntok * dk * es);
   const Span sb = span(beta, ntok * es);
@@ -113,12 +166,88 @@ extern "C" kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* 
     if (initial_state && overlaps(sc, span(initial_state, state_bytes))) return KDA_ERR_ALIAS;
     if (final_state && overlaps(sc, span(final_state, state_bytes))) return KDA_ERR_ALIAS;
   }
+  if (ws_need > 0) {
+    const Span sw = span(workspace, (int64_t)ws_need);
+    for (const Span& s : inputs)
+      if (overlaps(sw, s)) return KDA_ERR_ALIAS;
+    if (overlaps(sw, so)) return KDA_ERR_ALIAS;
+    if (initial_state && overlaps(sw, span(initial_state, state_bytes))) return KDA_ERR_ALIAS;
+    if (final_state && overlaps(sw, span(final_state, state_bytes))) return KDA_ERR_ALIAS;
+    if (checkpoints && overlaps(sw, span(checkpoints, B * (T / checkpoint_every) * H * dk * dv * 4)))
+      return KDA_ERR_ALIAS;
+  }
 
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, o, final_state,
-                     checkpoint_every ? checkpoints : nullptr, B, T, H, checkpoint_every};
-  const hipError_t e = kda::chunk_fwd(a, dk, dv, in == KDA_BF16, out == KDA_BF16,
-                                      reinterpret_cast<hipStream_t>(stream));
+                     checkpoint_every ? checkpoints : nullptr, B, T, H, checkpoint_every,
+                     nseg > 1 ? seg_len : T, nseg, 0, nullptr, nullptr, nullptr};
+  if (nseg > 1) {
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* seg_in = reinterpret_cast<float*>(ws);
+    float* seg_z = reinterpret_cast<float*>(ws + off_z);
+    float* seg_p = reinterpret_cast<float*>(ws + off_p);
+    kda::PrefillArgs s1 = a;
+    s1.mode = 1;
+    s1.seg_z = seg_z;
+    s1.seg_p = seg_p;
+    hipError_t e = kda::chunk_fwd(s1, dk, dv, bf16, out == KDA_BF16, st);
+    if (e == hipSuccess)
+      e = kda::segment_scan(initial_state, seg_z, seg_p, seg_in, B, H, nseg, dk, dv, st);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    a.seg_in = seg_in;
+  }
+  const hipError_t e = kda::chunk_fwd(a, dk, dv, bf16, out == KDA_BF16, st);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int64_t kda_chunk_fwd_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                                int chunk, kda_dtype_t in) {
+  if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return 0;
+  return auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16);
+}
+
+extern "C" size_t kda_chunk_fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk,
+                                                          int dv, int chunk, kda_dtype_t in,
+                                                          int64_t segment_tokens) {
+  if (!sizes_ok(B, T, H, dk, dv, chunk, in) || segment_tokens < 1 || segment_tokens % chunk != 0)
+    return 0;
+  const int64_t nseg = num_segments(T, segment_tokens);
+  if (!mul_ok(B * H, nseg) || !mul_ok(B * H * nseg, (int64_t)dk * (2 * dv + dk) * 4)) return 0;
+  return segment_workspace(B, H, nseg, dk, dv, nullptr, nullptr);
+}
+
+extern "C" size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                                int chunk, kda_dtype_t in) {
+  if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return 0;
+  return kda_chunk_fwd_segmented_workspace_bytes(
+      B, T, H, dk, dv, chunk, in, auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16));
+}
+
+extern "C" kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                                      const void* beta, const float* initial_state, void* o,
+                                      float* final_state, float* checkpoints,
+                                      int64_t checkpoint_every, int64_t B, int64_t T, int64_t H,
+                                      int dk, int dv, int chunk, kda_dtype_t in, kda_dtype_t out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          : kChunk;
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
+                        checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
+                        workspace_bytes, stream);
+}
+
+extern "C" kda_status_t kda_chunk_fwd_segmented(
+    const void* q, const void* k, const void* v, const void* g, const void* beta,
+    const float* initial_state, void* o, float* final_state, float* checkpoints,
+    int64_t checkpoint_every, int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+    kda_dtype_t in, kda_dtype_t out, int64_t segment_tokens, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
+                        checkpoint_every, B, T, H, dk, dv, chunk, in, out, segment_tokens,
+                        workspace, workspace_bytes, stream);
 }
 
 extern "C" kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v,

@@ -6,6 +6,17 @@
 
 namespace kda {
 
+// One launch of the fused chunk kernel.  The sequence of each (b, h) is cut
+// into nseg segments of seg_len tokens (the last one may be shorter); every
+// (b, segment, h) is walked by its own workgroups.
+//   mode 0 (outputs): segment j starts from initial state s0 when nseg == 1,
+//     else from seg_in[b, j, h]; o and checkpoints are written, and the last
+//     segment writes s_final.
+//   mode 1 (segment summaries, segments 0..nseg-2): "Z" workgroups run the
+//     segment from a zero state (segment 0 from s0) and store the state at its
+//     end in seg_z[b, j, h] (dk x dv); "P" workgroups (segments >= 1) run it
+//     with v = 0 from the identity and store the segment's transition matrix in
+//     seg_p[b, j, h] (dk x dk).  Nothing else is written.
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -17,13 +28,28 @@ struct PrefillArgs {
   float* s_final;
   float* ck;
   int64_t B, T, H, ck_every;
+  int64_t seg_len, nseg;
+  int mode;
+  const float* seg_in;
+  float* seg_z;
+  float* seg_p;
 };
 
-// Number of workgroups the prefill launch uses for B*H heads (fits int32 or not).
-int64_t prefill_grid(int64_t heads, int dk, int dv, bool in_bf16);
+// d_v slice width per prefill workgroup.
+int prefill_slice(int dk, int dv, bool in_bf16);
+
+// Number of workgroups of one prefill launch over `units` (b, segment, h)
+// triples with `slices` workgroups each.
+int64_t prefill_grid(int64_t units, int slices);
 
 hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool out_bf16,
                      hipStream_t s);
+
+// Entry states of the segments: seg_in[b, 0, h] = s0 (zeros if NULL),
+// seg_in[b, 1, h] = seg_z[b, 0, h], seg_in[b, j+1, h] = seg_p[b, j, h] seg_in[b, j, h]
+// + seg_z[b, j, h].  float32 throughout.
+hipError_t segment_scan(const float* s0, const float* seg_z, const float* seg_p, float* seg_in,
+                        int64_t B, int64_t H, int64_t nseg, int dk, int dv, hipStream_t s);
 
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int64_t nh, int dk, int dv,

@@ -193,18 +193,27 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   const int rt = wave & 3;            // row tile of the chunk owned by this wave
   const int jt0 = (wave >> 2) * NJW;  // its first value-column tile
 
-  // Workgroup -> (head, slice): consecutive workgroups are dealt round-robin to
-  // the 8 XCDs, so give all slices of a head the same XCD (and L2).
-  const int64_t nheads = p.B * p.H;
+  // Workgroup -> (unit, slice), unit = (b, segment, h): consecutive workgroups
+  // are dealt round-robin to the 8 XCDs, so give all slices of a unit the same
+  // XCD (and L2).  The summary pass (mode 1) adds DK / DVS slices that carry
+  // the segment's transition matrix, and covers every segment but the last.
+  constexpr int NPSL = DK / DVS;
+  const int nsl = p.mode ? NSLICE + NPSL : NSLICE;
+  const int64_t nsg = p.mode ? p.nseg - 1 : p.nseg;
   const int64_t x = blockIdx.x;
-  const int64_t grp = x / (8 * NSLICE);
-  const int gi = (int)(x % (8 * NSLICE));
-  const int64_t head = grp * 8 + (gi % 8);
+  const int64_t grp = x / (8 * nsl);
+  const int gi = (int)(x % (8 * nsl));
+  const int64_t unit = grp * 8 + (gi % 8);
   const int slice = gi / 8;
-  if (head >= nheads) return;
-  const int64_t b = head / p.H, h = head % p.H;
-  const int j0 = slice * DVS;
+  if (unit >= p.B * nsg * p.H) return;
+  const int64_t h = unit % p.H, bj = unit / p.H, seg = bj % nsg, b = bj / nsg;
+  const bool pmode = slice >= NSLICE;  // transition workgroup (mode 1 only)
+  if (pmode && seg == 0) return;       // segment 0's transition is never used
+  const int j0 = (pmode ? slice - NSLICE : slice) * DVS;
   const int64_t T = p.T, H = p.H;
+  const int64_t tb = seg * p.seg_len;                             // first token
+  const int64_t te = (T - tb) < p.seg_len ? T : tb + p.seg_len;   // one past the last
+  const bool emit = p.mode == 0;
 
   const TIn* gq = reinterpret_cast<const TIn*>(p.q);
   const TIn* gk = reinterpret_cast<const TIn*>(p.k);
@@ -212,9 +221,15 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   const TIn* gg = reinterpret_cast<const TIn*>(p.g);
   const TIn* gb = reinterpret_cast<const TIn*>(p.beta);
   TOut* go = reinterpret_cast<TOut*>(p.o);
-  const int64_t state_off = head * (int64_t)DK * DV;
+  const int64_t head_off = (b * H + h) * (int64_t)DK * DV;       // [B, H, DK, DV] states
+  const int64_t seg_unit = (b * p.nseg + seg) * H + h;           // [B, nseg, H, ...] states
 
   // ---- state slice in accumulators: tiles tt = SPW*wave + i -> (ct, jt)
+  const float* src = nullptr;  // entry state (row stride DV), NULL = zeros
+  if (emit)
+    src = p.nseg > 1 ? p.seg_in + seg_unit * DK * DV : (p.s0 ? p.s0 + head_off : nullptr);
+  else if (seg == 0 && p.s0)
+    src = p.s0 + head_off;
   f32x4 Sacc[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
@@ -222,7 +237,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int c = 16 * ct + 4 * lg + m, jv = 16 * jt + l16;
-      Sacc[i][m] = p.s0 ? p.s0[state_off + (int64_t)c * DV + j0 + jv] : 0.f;
+      if (pmode)
+        Sacc[i][m] = (c == j0 + jv) ? 1.f : 0.f;  // identity columns j0..j0+DVS-1
+      else
+        Sacc[i][m] = src ? src[(int64_t)c * DV + j0 + jv] : 0.f;
     }
   }
   auto store_state_operand = [&]() {
@@ -242,7 +260,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // 8 consecutive tokens of one value column, raw bits in 32-bit containers (no
   // packing at load time, which would wait for the loads)
   typedef typename std::conditional<sizeof(TIn) == 2, uint16_t, uint32_t>::type raw_t;
-  uint32_t pv[8];
+  uint32_t pv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // stays zero for transition workgroups
   TIn pbeta = from_f32<TIn>(0.f);  // kept raw: converting here would wait for the load
   // token strides (elements); offsets inside one chunk fit in 32 bits
   const uint32_t rs_k = (uint32_t)(H * DK), rs_v = (uint32_t)(H * DV), rs_b = (uint32_t)H;
@@ -252,10 +270,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // the memory pipeline is not asked for a whole chunk at once.
   auto prefetch = [&](int64_t t0, int part) {
     const int64_t cb = (b * T + t0) * H + h;
-    const int last = (int)((T - t0) < kC ? (T - t0) : kC) - 1;
+    const int last = (int)((te - t0) < kC ? (te - t0) : kC) - 1;
     if (part == 0) {
       const TIn* vb = gv + cb * DV + j0;
-      if (tid < NVT) {
+      if (tid < NVT && !pmode) {
         const int jv = tid % DVS, r0v = 8 * (tid / DVS);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -282,7 +300,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // (float32); v^T; beta.  Rows past the end become beta = 0, g = 0, k = q = v = 0
   // tokens, which leave the state unchanged.
   auto stage = [&](int64_t t0) {
-    const int nvalid = (int)((T - t0) < kC ? (T - t0) : kC);
+    const int nvalid = (int)((te - t0) < kC ? (te - t0) : kC);
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
       const int pc = tid + NT * i;
@@ -320,13 +338,13 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     if (tid < kC) sBeta[tid] = (tid < nvalid) ? to_f32(pbeta) : 0.f;
   };
 
-  const int64_t nchunks = (T + kC - 1) / kC;
-  for (int part = 0; part < 4; ++part) prefetch(0, part);
-  stage(0);
+  const int64_t nchunks = (te - tb + kC - 1) / kC;
+  for (int part = 0; part < 4; ++part) prefetch(tb, part);
+  stage(tb);
   __syncthreads();
 
   for (int64_t n = 0; n < nchunks; ++n) {
-    const int64_t t0 = n * kC;
+    const int64_t t0 = tb + n * kC;
     refresh_lane();
     // Next chunk's inputs: loaded while this chunk computes, staged at its end.  The
     // last chunk reloads itself (in bounds, never used) so that loads and staging
@@ -693,10 +711,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     store_state_operand();  // only the row-tile phase reads it, and that phase is over
     __syncthreads();
     stage(tn);
-    {  // output: one 16-byte store per piece, rows of DVS contiguous values
+    if (emit) {  // output: one 16-byte store per piece, rows of DVS contiguous values
       constexpr int PPR = DVS * (int)sizeof(TOut) / 16;  // 16-byte pieces per row
       const int64_t ob = ((b * T + t0) * H + h) * DV + j0;
-      const int nvalid = (int)((T - t0) < kC ? (T - t0) : kC);
+      const int nvalid = (int)((te - t0) < kC ? (te - t0) : kC);
 #pragma unroll
       for (int pc = tid; pc < kC * PPR; pc += NT) {
         const int r = pc / PPR, c = (pc % PPR) * (16 / (int)sizeof(TOut));
@@ -706,8 +724,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       }
     }
 
-    if (p.ck && ((n + 1) * kC) % p.ck_every == 0 && (n + 1) * kC <= T) {
-      const int64_t nck = T / p.ck_every, idx = (n + 1) * kC / p.ck_every - 1;
+    if (emit && p.ck && (t0 + kC) % p.ck_every == 0 && t0 + kC <= te) {
+      const int64_t nck = T / p.ck_every, idx = (t0 + kC) / p.ck_every - 1;
       float* dst = p.ck + ((b * nck + idx) * H + h) * (int64_t)DK * DV;
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
@@ -720,14 +738,25 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     __syncthreads();
   }
 
-  if (p.s_final) {
+  // state at the end of the walk: the final state (last segment of mode 0), or
+  // the segment summary (mode 1; transitions have row stride DK)
+  float* dst = nullptr;
+  int64_t ld = DV;
+  if (emit) {
+    if (seg == p.nseg - 1 && p.s_final) dst = p.s_final + head_off;
+  } else if (pmode) {
+    dst = p.seg_p + seg_unit * DK * DK;
+    ld = DK;
+  } else {
+    dst = p.seg_z + seg_unit * DK * DV;
+  }
+  if (dst) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
       const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        p.s_final[state_off + (int64_t)(16 * ct + 4 * lg + m) * DV + j0 + 16 * jt + l16] =
-            Sacc[i][m];
+        dst[(int64_t)(16 * ct + 4 * lg + m) * ld + j0 + 16 * jt + l16] = Sacc[i][m];
     }
   }
 }
@@ -739,24 +768,21 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      Lay::TOTAL);
   if (e != hipSuccess) return e;
-  constexpr int NSLICE = DV / DVS;
-  const int64_t nheads = a.B * a.H;
-  const int64_t groups = (nheads + 7) / 8;
-  const int64_t grid = groups * 8 * NSLICE;
+  constexpr int NSLICE = DV / DVS, NPSL = DK / DVS;
+  const int64_t units = a.B * (a.mode ? a.nseg - 1 : a.nseg) * a.H;
+  const int64_t grid = prefill_grid(units, a.mode ? NSLICE + NPSL : NSLICE);
   kern<<<dim3((unsigned)grid), dim3(512), Lay::TOTAL, stream>>>(a);
   return hipGetLastError();
 }
 
 // d_v slice width per workgroup (must match the instantiations in chunk_fwd).
-static int prefill_slice(int dk, int dv, bool in_bf16) {
+int prefill_slice(int dk, int dv, bool in_bf16) {
   (void)dv;
   if (!in_bf16) return 64;
   return dk == 128 ? 64 : 32;
 }
 
-int64_t prefill_grid(int64_t heads, int dk, int dv, bool in_bf16) {
-  return ((heads + 7) / 8) * 8 * (dv / prefill_slice(dk, dv, in_bf16));
-}
+int64_t prefill_grid(int64_t units, int slices) { return ((units + 7) / 8) * 8 * slices; }
 
 hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool out_bf16,
                      hipStream_t s) {

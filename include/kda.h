@@ -65,8 +65,9 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_str(kda_status_t status);
 
-/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none).
- * Returns 0 as well for unsupported sizes; kda_chunk_fwd then reports why. */
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if none:
+ * one segment, see kda_chunk_fwd_segment_tokens).  Returns 0 as well for
+ * unsupported sizes; kda_chunk_fwd then reports why. */
 size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
                                      kda_dtype_t in);
 
@@ -93,7 +94,13 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, in
  *                 Entry j is the state after token checkpoint_every*(j+1).
  *   checkpoint_every  0 = off; else a positive multiple of `chunk`.
  *   workspace / workspace_bytes  at least kda_chunk_fwd_workspace_bytes(...)
- *                 bytes (may be NULL when that is 0).
+ *                 bytes (may be NULL when that is 0), else KDA_ERR_WORKSPACE.
+ *                 Must not overlap any other buffer.
+ *
+ * When B * H heads are too few to occupy the GPU, the sequences are cut into
+ * segments (kda_chunk_fwd_segment_tokens reports the length) and the call
+ * proceeds as kda_chunk_fwd_segmented below; the workspace holds the segments'
+ * summaries and entry states.
  *
  * T need not be a multiple of `chunk`: the tail is padded inside the kernel
  * with beta = 0, g = 0 tokens, which leave the state unchanged.
@@ -104,6 +111,52 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const vo
                            int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
                            kda_dtype_t in, kda_dtype_t out, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd_segmented - kda_chunk_fwd with the sequence cut into segments.
+ *
+ * Same arguments, outputs and errors as kda_chunk_fwd, plus `segment_tokens`
+ * (a positive multiple of `chunk`).  Each sequence is cut into
+ * ceil(T / segment_tokens) segments; segment_tokens >= T is one segment, the
+ * same computation as kda_chunk_fwd's single pass.  With several segments
+ * three launches are enqueued:
+ *   1. every segment but the last is summarised in parallel: Z, the state it
+ *      reaches from a zero state (the first segment starts from initial_state),
+ *      and P (dk x dk), the product of its tokens' transitions, obtained by
+ *      running it from the identity with v = 0;
+ *   2. a prefix scan over segments, S_in(j+1) = P_j S_in(j) + Z_j, gives every
+ *      segment's entry state;
+ *   3. every segment is run from its entry state, writing o, checkpoints and
+ *      (last segment) final_state.
+ * The segment law is the one the orkas.ai blog "Kimi K3 architecture" states
+ * for splitting a sequence across devices (section "The cost is paid in the
+ * serving stack"); here it spreads few long sequences over the GPU's compute
+ * units.  The results agree with the one-segment path to within rounding (not
+ * bitwise: the summaries take a different order of operations).
+ *
+ *   workspace / workspace_bytes  at least
+ *                 kda_chunk_fwd_segmented_workspace_bytes(...) bytes (NULL
+ *                 allowed when that is 0); must not overlap any other buffer.
+ */
+kda_status_t kda_chunk_fwd_segmented(const void* q, const void* k, const void* v, const void* g,
+                                     const void* beta, const float* initial_state, void* o,
+                                     float* final_state, float* checkpoints,
+                                     int64_t checkpoint_every, int64_t B, int64_t T, int64_t H,
+                                     int dk, int dv, int chunk, kda_dtype_t in, kda_dtype_t out,
+                                     int64_t segment_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kda_chunk_fwd_segmented for these sizes: 4 * B * nseg * H
+ * * dk * (2 dv + dk) rounded up, 0 for one segment or unsupported sizes. */
+size_t kda_chunk_fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, int dv,
+                                               int chunk, kda_dtype_t in,
+                                               int64_t segment_tokens);
+
+/* The segment length kda_chunk_fwd uses for these sizes (a multiple of 64; a
+ * value >= T means one segment), or 0 for unsupported sizes.  Several segments
+ * are chosen only when B * H is too small to occupy the GPU's compute units. */
+int64_t kda_chunk_fwd_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+                                     kda_dtype_t in);
 
 /*
  * kda_recurrent_step - one decode step for N independent sequences.

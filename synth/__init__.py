@@ -59,7 +59,7 @@ class Workload:
     dv: int
     chunk: int
     dtype: str  # "f32" or "bf16": storage dtype of q, k, v, g, beta
-    a_law: str  # "n02" = N(0, 2), "n51" = N(5, 1), "mixed" = half/half
+    a_law: str  # "n02" = N(0, 2), "n51" = N(5, 1), "mixed" = half/half, "slow" = N(-7, 1)
     init_state: bool
     seed: int
 
@@ -114,6 +114,10 @@ def _decay_logits(rng: np.random.Generator, shape, a_law: str) -> np.ndarray:
         return rng.normal(0.0, _SQRT2, shape)
     if a_law == "n51":
         return rng.normal(5.0, 1.0, shape)
+    if a_law == "slow":
+        # long memory (g ~ -1e-3 per token): a state carries across thousands of
+        # tokens, so long-range hand-offs are exercised, not erased by the decay
+        return rng.normal(-7.0, 1.0, shape)
     if a_law == "mixed":
         d = shape[-1]
         a = rng.normal(0.0, _SQRT2, shape)
@@ -232,6 +236,8 @@ def device_prefill_inputs(w: Workload, device, seed_offset: int = 0):
         a.mul_(_SQRT2)
     elif w.a_law == "n51":
         a.add_(5.0)
+    elif w.a_law == "slow":
+        a.sub_(7.0)
     else:
         a[..., : dk // 2].mul_(_SQRT2)
         a[..., dk // 2:].add_(5.0)

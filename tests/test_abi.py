@@ -36,8 +36,30 @@ def test_status_strings(lib):
     assert lib.kda_status_str(99).decode() == "KDA_ERR_UNKNOWN"
 
 
-def test_workspace_is_zero(lib):
-    assert lib.kda_chunk_fwd_workspace_bytes(4, 4096, 32, 128, 128, 64, kda.KDA_BF16) == 0
+def test_workspace_sizes(lib):
+    bf = kda.KDA_BF16
+    # 128 heads fill the GPU: one segment, no workspace
+    assert lib.kda_chunk_fwd_segment_tokens(4, 4096, 32, 128, 128, 64, bf) >= 4096
+    assert lib.kda_chunk_fwd_workspace_bytes(4, 4096, 32, 128, 128, 64, bf) == 0
+    # few heads, long sequences: several segments, workspace = entry + zero-start states
+    # [B, nseg, H, dk, dv] and transitions [B, nseg, H, dk, dk], float32
+    for B, T, H, dk, dv in [(1, 65536, 32, 128, 128), (1, 1 << 20, 16, 128, 128),
+                            (1, 32768, 8, 64, 128)]:
+        seg = lib.kda_chunk_fwd_segment_tokens(B, T, H, dk, dv, 64, bf)
+        assert 0 < seg < T and seg % 64 == 0
+        nseg = -(-T // seg)
+        want = 4 * B * nseg * H * dk * (2 * dv + dk)
+        got = lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, 64, bf)
+        assert want <= got < want + 3 * 256
+        assert got == lib.kda_chunk_fwd_segmented_workspace_bytes(B, T, H, dk, dv, 64, bf, seg)
+    # explicit segment lengths
+    assert lib.kda_chunk_fwd_segmented_workspace_bytes(1, 256, 2, 64, 64, 64, kda.KDA_F32, 256) == 0
+    assert lib.kda_chunk_fwd_segmented_workspace_bytes(1, 256, 2, 64, 64, 64, kda.KDA_F32,
+                                                       64) == 4 * 4 * 2 * 64 * 192
+    assert lib.kda_chunk_fwd_segmented_workspace_bytes(1, 256, 2, 64, 64, 64, kda.KDA_F32, 100) == 0
+    # unsupported sizes
+    assert lib.kda_chunk_fwd_segment_tokens(1, 256, 2, 96, 64, 64, bf) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 2, 96, 64, 64, bf) == 0
 
 
 FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
@@ -69,6 +91,31 @@ def test_chunk_fwd_rejects_before_launch(lib):
     assert _fwd(lib, o=2 * FAKE + 64) == -6  # o inside k
     assert _fwd(lib, o=o, sf=o + 128) == -6  # final state overlaps o
     assert _fwd(lib, o=o, s0=80 * FAKE, sf=80 * FAKE + 16) == -6  # partial state overlap
+
+
+def _seg(lib, seg, ws=None, ws_bytes=0, **kw):
+    a = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, s0=None, o=64 * FAKE,
+             sf=None, ck=None, every=0, B=1, T=256, H=1, dk=128, dv=128, chunk=64,
+             din=kda.KDA_BF16, dout=kda.KDA_BF16)
+    a.update(kw)
+    return lib.kda_chunk_fwd_segmented(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"],
+                                       a["sf"], a["ck"], a["every"], a["B"], a["T"], a["H"],
+                                       a["dk"], a["dv"], a["chunk"], a["din"], a["dout"], seg, ws,
+                                       ws_bytes, None)
+
+
+def test_segmented_rejects_before_launch(lib):
+    need = lib.kda_chunk_fwd_segmented_workspace_bytes(1, 256, 1, 128, 128, 64, kda.KDA_BF16, 64)
+    assert need > 0
+    ws = 128 * FAKE
+    assert _seg(lib, 0, ws, need) == -2
+    assert _seg(lib, 100, ws, need) == -2
+    assert _seg(lib, 64) == -5  # no workspace
+    assert _seg(lib, 64, ws, need - 1) == -5
+    assert _seg(lib, 64, ws + 8, need) == -4
+    assert _seg(lib, 64, 64 * FAKE + 256, need) == -6  # workspace inside o
+    assert _seg(lib, 64, 2 * FAKE, need) == -6  # workspace inside k
+    assert _seg(lib, 64, ws, need, q=None) == -1
 
 
 def _step(lib, **kw):

@@ -27,12 +27,13 @@ def test_split_at_chunk_boundary_matches_monolithic(dtype):
                                        dk=64 if dtype == "f32" else 128,
                                        dv=64 if dtype == "f32" else 128)
     d = _inputs(w)
-    o, sf, _ = _fwd(d)
+    one = 1 << 40  # one segment: the single pass of the chunk kernel
+    o, sf, _ = _fwd(d, segment_tokens=one)
     cut = 192
     first = {n: d[n][:, :cut].contiguous() for n in ("q", "k", "v", "g", "beta")}
     rest = {n: d[n][:, cut:].contiguous() for n in ("q", "k", "v", "g", "beta")}
-    o1, s1, _ = _fwd(dict(first, s0=d["s0"]))
-    o2, s2, _ = _fwd(dict(rest, s0=s1))
+    o1, s1, _ = _fwd(dict(first, s0=d["s0"]), segment_tokens=one)
+    o2, s2, _ = _fwd(dict(rest, s0=s1), segment_tokens=one)
     torch.cuda.synchronize()
     # same arithmetic per chunk, so the hand-off is exact
     assert torch.equal(torch.cat([o1, o2], 1), o) and torch.equal(s2, sf)
@@ -80,8 +81,8 @@ def test_padding_with_no_op_tokens_is_neutral():
             z = np.random.default_rng(0).standard_normal(z.shape)
         y[n] = np.concatenate([x[n], z], axis=1)
     y["s0"] = x["s0"]
-    a = _fwd(synth.to_torch(x, w.dtype, DEV))
-    b = _fwd(synth.to_torch(y, w.dtype, DEV))
+    a = _fwd(synth.to_torch(x, w.dtype, DEV), segment_tokens=1 << 40)
+    b = _fwd(synth.to_torch(y, w.dtype, DEV), segment_tokens=1 << 40)
     torch.cuda.synchronize()
     assert torch.allclose(a[1], b[1], rtol=0, atol=1e-6 * float(a[1].abs().max()))
     assert torch.equal(a[0], b[0][:, :130])

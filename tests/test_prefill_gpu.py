@@ -27,7 +27,7 @@ def _ref(x, every=0):
     return o, s, ck
 
 
-def _check(w, out_dtype=None, every=0):
+def _check(w, out_dtype=None, every=0, tol=None):
     x = synth.prefill_inputs(w)
     print(f"[prefill] {w.name} B{w.B} T{w.T} H{w.H} dk{w.dk} dv{w.dv} {w.dtype} "
           f"out={out_dtype}", flush=True)
@@ -35,7 +35,7 @@ def _check(w, out_dtype=None, every=0):
     o_r, s_r, ck_r = _ref(x, every)
     e_o, e_s = oracle.rel_l2(o, o_r), oracle.rel_l2(s, s_r)
     print(f"[prefill]   rel_l2 o {e_o:.3e} state {e_s:.3e}", flush=True)
-    tol = TOL[w.dtype]
+    tol = TOL[w.dtype] if tol is None else tol
     assert e_o <= tol and e_s <= tol, (e_o, e_s)
     if every:
         assert oracle.rel_l2(ck, ck_r) <= tol
@@ -60,6 +60,15 @@ def test_bf16_small_shapes(dk, dv):
 def test_bf16_laws_bf16_out(law):
     w = synth.PREFILL_B4_T4096.replace(B=1, T=1024 + 37, H=4, a_law=law)
     _check(w)
+
+
+def test_bf16_long_memory_fp32_out():
+    """Decay logits ~ N(-7, 1) (long memory, outside the pages' workloads).  The rounding
+    of the single-bfloat16 operands accumulates; a float64 model of the chunked algorithm
+    with the kernel's roundings predicts about 3.2e-3 at 4096 tokens, so the bound here
+    is 5e-3."""
+    w = synth.PREFILL_B4_T4096.replace(B=1, T=4096, H=4, a_law="slow")
+    _check(w, out_dtype=torch.float32, tol=5e-3)
 
 
 def test_checkpoints_match_oracle():
