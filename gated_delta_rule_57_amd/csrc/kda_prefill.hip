@@ -99,24 +99,29 @@ struct PrefillLayout {
 
   static constexpr int SZ_K = kC * LDK * OPB;
   static constexpr int SZ_Q2 = BF16 ? kC * LDK * OPB : 0;
-  static constexpr int SZ_L = kC * LDF * 4;
-  static constexpr int SZ_KCT = DK * LDC * OPB;
+  // gamma (float32) during the scan; then the column operand k 2^-L, as float32
+  // (float32 inputs) or as a hi + lo pair of bfloat16 arrays
+  static constexpr int SZ_L = (BF16 && 2 * kC * LDK * OPB > kC * LDF * 4) ? 2 * kC * LDK * OPB
+                                                                         : kC * LDF * 4;
+  static constexpr int SZ_KBT = DK * LDC * OPB;
   static constexpr int SZ_QC = kC * LDK * OPB;
   static constexpr int SZ_TF = kC * LDA * 4;
   static constexpr int SZ_TB = kC * LDC * OPB;
   static constexpr int SZ_UT = (BF16 ? 2 : 1) * DVS * LDC * OPB;
   static constexpr int PH1 = 2 * SZ_K + SZ_Q2 + SZ_L;
-  static constexpr int PH2 = 2 * SZ_KCT + SZ_QC + SZ_TB + SZ_TF;
+  static constexpr int PH2 = 2 * SZ_QC + SZ_KBT + SZ_TB + SZ_TF;
   static constexpr int REGION = PH1 > PH2 ? PH1 : PH2;
   // phase-1 view of the shared region: raw inputs, then the A/P operands
   static constexpr int O_K = 0, O_Q = SZ_K, O_Q2 = 2 * SZ_K, O_L = 2 * SZ_K + SZ_Q2;
   // phase-2 view: T float32 last, so that U^T can take its place (and the slack)
-  static constexpr int O_KCT = 0, O_TB = SZ_KCT, O_QC = O_TB + SZ_TB, O_KBT = O_QC + SZ_QC;
-  static constexpr int O_TF = O_KBT + SZ_KCT;
+  static constexpr int O_KC = 0, O_TB = SZ_QC, O_QC = O_TB + SZ_TB, O_KBT = O_QC + SZ_QC;
+  static constexpr int O_TF = O_KBT + SZ_KBT;
   static constexpr int O_UT = O_TF;
   static_assert(O_UT + SZ_UT <= REGION, "U^T must fit over T and the slack");
   // buffers outside the region
-  static constexpr int SZ_AW = (kC * LDA * 4 > kC * LDK * OPB) ? kC * LDA * 4 : kC * LDK * OPB;
+  // A (float32), then Z^T (hi + lo for bfloat16), then the output staging
+  static constexpr int SZ_ZT = (BF16 ? 2 : 1) * DVS * LDC * OPB;
+  static constexpr int SZ_AW = (kC * LDA * 4 > SZ_ZT) ? kC * LDA * 4 : SZ_ZT;
   static constexpr int O_A = REGION;  // A, then W
   static constexpr int O_P = O_A + SZ_AW;
   static constexpr int O_VT = O_P + kC * LDA * 4;
@@ -159,7 +164,9 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   op_t* sQ = reinterpret_cast<op_t*>(smem + Lay::O_Q);
   op_t* sQ2 = reinterpret_cast<op_t*>(smem + Lay::O_Q2);
   float* sL = reinterpret_cast<float*>(smem + Lay::O_L);
-  op_t* sKcT = reinterpret_cast<op_t*>(smem + Lay::O_KCT);
+  op_t* sKdH = reinterpret_cast<op_t*>(smem + Lay::O_L);  // k 2^-L, hi part (bfloat16 inputs)
+  op_t* sKdL = sKdH + kC * LDK;                            // lo part
+  op_t* sKc = reinterpret_cast<op_t*>(smem + Lay::O_KC);
   op_t* sTb = reinterpret_cast<op_t*>(smem + Lay::O_TB);
   op_t* sQc = reinterpret_cast<op_t*>(smem + Lay::O_QC);
   op_t* sKbT = reinterpret_cast<op_t*>(smem + Lay::O_KBT);
@@ -167,7 +174,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   op_t* sUT = reinterpret_cast<op_t*>(smem + Lay::O_UT);
   op_t* sUT2 = sUT + DVS * LDC;  // lo part (bf16 only)
   float* sA = reinterpret_cast<float*>(smem + Lay::O_A);
-  op_t* sW = reinterpret_cast<op_t*>(smem + Lay::O_A);
+  op_t* sZT = reinterpret_cast<op_t*>(smem + Lay::O_A);
+  op_t* sZT2 = sZT + DVS * LDC;  // lo part (bf16 only)
   float* sP = reinterpret_cast<float*>(smem + Lay::O_P);
   op_t* sVT = reinterpret_cast<op_t*>(smem + Lay::O_VT);
   op_t* sST = reinterpret_cast<op_t*>(smem + Lay::O_ST);
@@ -424,7 +432,13 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
           const op_t qh = from_f32<op_t>(qr);
           sQ[r * LDK + cc] = qh;
           if constexpr (BF16) sQ2[r * LDK + cc] = from_f32<op_t>(qr - to_f32(qh));
-          sL[r * LDF + cc] = kd;
+          if constexpr (BF16) {
+            const op_t kh = from_f32<op_t>(kd);
+            sKdH[r * LDK + cc] = kh;
+            sKdL[r * LDK + cc] = from_f32<op_t>(kd - to_f32(kh));
+          } else {
+            sL[r * LDF + cc] = kd;
+          }
           dKc[e / 8][e % 8] = from_f32<op_t>(kr * eref);
           dQc[e / 8][e % 8] = from_f32<op_t>(qr * eref);
           dKb[e / 8][e % 8] = from_f32<op_t>(kd * ebar);
@@ -434,12 +448,16 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     __syncthreads();
 
     prefetch(tn, 2);
-    // ---- A and P tiles, every tile pair one dense product
-    for (int pi = wave; pi < 10; pi += NW) {
-      // pair order (R, I): (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-      const int R = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
-      const int I = pi - R * (R + 1) / 2;
-      const float* pair = (I < R) ? sPair + (R * (R - 1) / 2 + I) * DK : nullptr;
+    // ---- A and P tiles, every tile pair one dense product.  Waves 0-3 take the six
+    // off-diagonal pairs (two, two, one, one); wave 4 + R takes the diagonal pair
+    // (R, R) and inverts I + A_RR right away, keeping the inverse in registers (the
+    // triangular factor's shared-memory slots alias operands other waves still read).
+    f32x4 Dinv = {0.f, 0.f, 0.f, 0.f};
+    // DIAG is a compile-time tag, so that each k-step is straight-line code whose
+    // shared-memory loads the compiler can issue ahead of the previous step's MFMAs.
+    auto tile_pair = [&](auto diag_tag, const int R, const int I) {
+      constexpr bool DIAG = decltype(diag_tag)::value;
+      const float* pair = sPair + (R * (R - 1) / 2 + I) * DK;  // used off the diagonal only
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
       const int row = kSub * R + l16, col = kSub * I + l16;
 #pragma unroll
@@ -447,30 +465,29 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         const int k0 = kk + kofs;
         const frag aK = M::ld(sK + row * LDK + k0);
         const frag aQ = M::ld(sQ + row * LDK + k0);
-        if constexpr (BF16) {
+        if constexpr (BF16 && DIAG) {
+          // diagonal tile: column operand straight from its hi / lo arrays; P takes
+          // the three products of the split pairs
           const frag aQ2 = M::ld(sQ2 + row * LDK + k0);
-          float cf[8];
-          load8(sL + col * LDF + k0, cf);
-          if (pair) {
-            float pf[8];
-            load8(pair + k0, pf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cf[e] *= pf[e];
-          }
-          frag bh, bl;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const __bf16 hh_ = (__bf16)cf[e];
-            bh[e] = hh_;
-            bl[e] = (__bf16)(cf[e] - (float)hh_);
-          }
+          const frag bh = M::ld(sKdH + col * LDK + k0), bl = M::ld(sKdL + col * LDK + k0);
           accA = M::mma(aK, bh, accA);
           accP = M::mma(aQ, bh, accP);
           accP = M::mma(aQ2, bh, accP);
           accP = M::mma(aQ, bl, accP);
+        } else if constexpr (BF16) {
+          // off-diagonal tile: hi part x the pair's decay 2^(ref_R - ref_I) (<= 1),
+          // one bfloat16 operand for both products
+          const frag raw = M::ld(sKdH + col * LDK + k0);
+          float pf[8];
+          load8(pair + k0, pf);
+          frag b;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = (__bf16)((float)raw[e] * pf[e]);
+          accA = M::mma(aK, b, accA);
+          accP = M::mma(aQ, b, accP);
         } else {
           float cf = sL[col * LDF + k0];
-          if (pair) cf *= pair[k0];
+          if constexpr (!DIAG) cf *= pair[k0];
           accA = M::mma(aK, cf, accA);
           accP = M::mma(aQ, cf, accP);
         }
@@ -478,56 +495,34 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = kSub * R + 4 * lg + m, i = col;
-        sA[r * LDA + i] = (i < r) ? sBeta[r] * accA[m] : 0.f;
-        sP[r * LDA + i] = (i <= r) ? accP[m] : 0.f;
+        sA[r * LDA + i] = (!DIAG || i < r) ? sBeta[r] * accA[m] : 0.f;
+        sP[r * LDA + i] = (!DIAG || i <= r) ? accP[m] : 0.f;
       }
-    }
-    // zero the tiles above the diagonal
-    for (int e = tid; e < 6 * 256; e += NT) {
-      const int u = e / 256, w = e % 256;
-      const int R = u < 3 ? 0 : u < 5 ? 1 : 2;
-      const int I = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
-      const int r = kSub * R + w / 16, i = kSub * I + w % 16;
-      sA[r * LDA + i] = 0.f;
-      sP[r * LDA + i] = 0.f;
-    }
-    __syncthreads();
-
-    prefetch(tn, 3);
-    // ---- deferred operands into the released region (channel-major threads):
-    // k 2^G and k 2^(G_end - G) transposed (token-contiguous), q 2^G row-major.
-#pragma unroll
-    for (int e = 0; e < RPC && cm; e += 8) {
-      const vec8 vc = dKc[e / 8], vb = dKb[e / 8];
-      if constexpr (BF16) {
-        *reinterpret_cast<vec8*>(sKcT + cc * LDC + r0 + e) = vc;
-        *reinterpret_cast<vec8*>(sKbT + cc * LDC + r0 + e) = vb;
-      } else {
-        *reinterpret_cast<f32x4*>(sKcT + cc * LDC + r0 + e) = f32x4{vc[0], vc[1], vc[2], vc[3]};
-        *reinterpret_cast<f32x4*>(sKcT + cc * LDC + r0 + e + 4) = f32x4{vc[4], vc[5], vc[6], vc[7]};
-        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e) = f32x4{vb[0], vb[1], vb[2], vb[3]};
-        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e + 4) = f32x4{vb[4], vb[5], vb[6], vb[7]};
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < RPC && cm; ++e) sQc[(r0 + e) * LDK + cc] = dQc[e / 8][e % 8];
-    for (int e = tid; e < 6 * 256; e += NT) {  // T' is lower triangular
-      const int u = e / 256, w = e % 256;
-      const int R = u < 3 ? 0 : u < 5 ? 1 : 2;
-      const int I = u < 3 ? u + 1 : u < 5 ? u - 1 : 3;
-      sTb[(kSub * R + w / 16) * LDC + kSub * I + w % 16] = from_f32<op_t>(0.f);
-    }
-
-    // ---- T = (I + A)^-1.  Diagonal blocks: wave R < 4 inverts I + A_RR in registers.
-    if (wave < kNSub) {
-      const int R = wave;
+      return accA;
+    };
+    if (wave < 4) {
+      // (1,0) (3,1) | (2,0) (3,2) | (2,1) | (3,0)
+      const int R0 = wave == 0 ? 1 : wave == 1 ? 2 : wave == 2 ? 2 : 3;
+      const int I0 = wave == 2 ? 1 : 0;
+      tile_pair(std::false_type{}, R0, I0);
+      if (wave < 2) tile_pair(std::false_type{}, 3, wave + 1);
+    } else {
+      const int R = wave - 4;
+      const f32x4 acc = tile_pair(std::true_type{}, R, R);
+      // Nd: this lane's entries of A_RR (rows 4 lg + m, column l16), as written to
+      // sA; Nt: the transposed entries, read back from sA (same wave, in order)
       f32x4 Nd, Nt, Id;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        Nd[m] = sA[(kSub * R + 4 * lg + m) * LDA + kSub * R + l16];
-        Nt[m] = sA[(kSub * R + l16) * LDA + kSub * R + 4 * lg + m];
-        Id[m] = (4 * lg + m == l16) ? 1.f : 0.f;
+        const int r = 4 * lg + m;
+        Nd[m] = (l16 < r) ? sBeta[kSub * R + r] * acc[m] : 0.f;
+        Id[m] = (r == l16) ? 1.f : 0.f;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Nt[m] = sA[(kSub * R + l16) * LDA + kSub * R + 4 * lg + m];
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       const f32x4 N2 = mm16(Nt, Nd, z), N2t = mm16(Nd, Nt, z);
       const f32x4 N4 = mm16(N2t, N2, z), N4t = mm16(N2, N2t, z);
@@ -535,13 +530,55 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       const f32x4 X1 = Id - Nd, X1t = Id - Nt;
       const f32x4 X2 = mm16(X1t, N2, X1), X2t = mm16(N2, X1t, X1t);
       const f32x4 X3 = mm16(X2t, N4, X2), X3t = mm16(N4, X2t, X2t);
-      const f32x4 D = mm16(X3t, N8, X3);
+      Dinv = mm16(X3t, N8, X3);  // (I + A_RR)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8)
+    }
+    // Of the tiles above the diagonal only (0,1) and (2,3) are ever read (by the
+    // row-tile products, whose k-steps span 32 tokens); A's are never read.
+    if (tid < 128) {
+      const int u = tid >> 6, w = tid & 63;
+      const int r = 32 * u + (w >> 2), i = 32 * u + kSub + 4 * (w & 3);
+      *reinterpret_cast<f32x4*>(sP + r * LDA + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+
+    prefetch(tn, 3);
+    // ---- deferred operands into the released region (channel-major threads):
+    // k 2^(G_end - G) transposed (token-contiguous), k 2^G and q 2^G row-major.
+#pragma unroll
+    for (int e = 0; e < RPC && cm; e += 8) {
+      const vec8 vb = dKb[e / 8];
+      if constexpr (BF16) {
+        *reinterpret_cast<vec8*>(sKbT + cc * LDC + r0 + e) = vb;
+      } else {
+        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e) = f32x4{vb[0], vb[1], vb[2], vb[3]};
+        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e + 4) = f32x4{vb[4], vb[5], vb[6], vb[7]};
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < RPC && cm; ++e) {
+      sKc[(r0 + e) * LDK + cc] = dKc[e / 8][e % 8];
+      sQc[(r0 + e) * LDK + cc] = dQc[e / 8][e % 8];
+    }
+    {  // T' is lower triangular; clear its upper tiles (0,1) and (2,3) (the ones read)
+      constexpr int EPP = 16 / Lay::OPB;        // elements per 16-byte piece
+      constexpr int PPR = kSub / EPP;           // pieces per tile row
+      if (tid < 2 * kSub * PPR) {
+        const int u = tid / (kSub * PPR), w = tid % (kSub * PPR);
+        const int r = 32 * u + w / PPR, i = 32 * u + kSub + EPP * (w % PPR);
+        *reinterpret_cast<uint4*>(sTb + r * LDC + i) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+
+    // ---- T = (I + A)^-1: the diagonal blocks computed with the A tiles go to shared
+    // memory now (float32 for the substitution below, times beta for T' = T Diag(beta))
+    if (wave >= 4) {
+      const int R = wave - 4;
       const float bcol = sBeta[kSub * R + l16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = kSub * R + 4 * lg + m;
-        sTf[r * LDA + kSub * R + l16] = D[m];
-        sTb[r * LDC + kSub * R + l16] = from_f32<op_t>(D[m] * bcol);
+        sTf[r * LDA + kSub * R + l16] = Dinv[m];
+        sTb[r * LDC + kSub * R + l16] = from_f32<op_t>(Dinv[m] * bcol);
       }
     }
     __syncthreads();
@@ -595,50 +632,70 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
-    // ---- per row tile: W = T' Kc (-> A's slot), U0 = T' V, U = U0 - W S, Qc S.
-    // Both waves of a row tile compute the whole W row tile (they need all of it
-    // as an operand) and store the same values.
+    // ---- per row tile, over the key channels: Y = Kc S and Qc S; Z = V - Y.  Then
+    // U = T' Z (= T' V - (T' Kc) S, the correction of the delta rule), which needs Z
+    // of the earlier row tiles: one barrier between.
     constexpr int NKT = kC / KS;  // k-steps over the chunk's tokens
     const int kend = 16 * rt + 16;  // T' and P rows of this tile vanish beyond kend
-    frag aT[NKT];
-#pragma unroll
-    for (int q = 0; q < NKT; ++q)
-      if (q * KS < kend) aT[q] = M::ld(sTb + (16 * rt + l16) * LDC + q * KS + kofs);
-#pragma unroll 4
-    for (int ct = 0; ct < DK / 16; ++ct) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < NKT; ++q)
-        if (q * KS < kend) acc = M::mma(aT[q], M::ld(sKcT + (16 * ct + l16) * LDC + q * KS + kofs), acc);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        sW[(16 * rt + 4 * lg + m) * LDK + 16 * ct + l16] = from_f32<op_t>(acc[m]);
-    }
     f32x4 Oacc[NJW];
     TOut* sO = reinterpret_cast<TOut*>(smem + Lay::O_A);  // [64][LDO] output staging
     constexpr int LDO = DVS + 16 / (int)sizeof(TOut);
     static_assert(kC * (DVS + 16 / (int)sizeof(TOut)) * (int)sizeof(TOut) <= Lay::SZ_AW, "O staging");
+    {
+      f32x4 y[NJW];
 #pragma unroll
-    for (int j = 0; j < NJW; ++j) {
-      const int jt = jt0 + j;
-      f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, ws = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < NKT; ++q)
-        if (q * KS < kend) u0 = M::mma(aT[q], M::ld(sVT + (16 * jt + l16) * LDC + q * KS + kofs), u0);
+      for (int j = 0; j < NJW; ++j) {
+        y[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int kk = 0; kk < DK; kk += KS) {
-        const frag bS = M::ld(sST + (16 * jt + l16) * LDK + kk + kofs);
-        ws = M::mma(M::ld(sW + (16 * rt + l16) * LDK + kk + kofs), bS, ws);
-        oq = M::mma(M::ld(sQc + (16 * rt + l16) * LDK + kk + kofs), bS, oq);
-      }
-      Oacc[j] = oq;
-      const int jv = 16 * jt + l16, i0 = 16 * rt + 4 * lg;
+        const frag aKc = M::ld(sKc + (16 * rt + l16) * LDK + kk + kofs);
+        const frag aQc = M::ld(sQc + (16 * rt + l16) * LDK + kk + kofs);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float u = u0[m] - ws[m];
-        const op_t uh = from_f32<op_t>(u);
-        sUT[jv * LDC + i0 + m] = uh;
-        if constexpr (BF16) sUT2[jv * LDC + i0 + m] = from_f32<op_t>(u - to_f32(uh));
+        for (int j = 0; j < NJW; ++j) {
+          const frag bS = M::ld(sST + (16 * (jt0 + j) + l16) * LDK + kk + kofs);
+          y[j] = M::mma(aKc, bS, y[j]);
+          Oacc[j] = M::mma(aQc, bS, Oacc[j]);
+        }
+      }
+      const int i0 = 16 * rt + 4 * lg;
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) {
+        const int jv = 16 * (jt0 + j) + l16;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float z = to_f32(sVT[jv * LDC + i0 + m]) - y[j][m];
+          const op_t zh = from_f32<op_t>(z);
+          sZT[jv * LDC + i0 + m] = zh;
+          if constexpr (BF16) sZT2[jv * LDC + i0 + m] = from_f32<op_t>(z - to_f32(zh));
+        }
+      }
+    }
+    __syncthreads();
+    {
+      frag aT[NKT];
+#pragma unroll
+      for (int q = 0; q < NKT; ++q)
+        if (q * KS < kend) aT[q] = M::ld(sTb + (16 * rt + l16) * LDC + q * KS + kofs);
+#pragma unroll
+      for (int j = 0; j < NJW; ++j) {
+        const int jt = jt0 + j;
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < NKT; ++q) {
+          if (q * KS < kend) {
+            u = M::mma(aT[q], M::ld(sZT + (16 * jt + l16) * LDC + q * KS + kofs), u);
+            if constexpr (BF16) u = M::mma(aT[q], M::ld(sZT2 + (16 * jt + l16) * LDC + q * KS + kofs), u);
+          }
+        }
+        const int jv = 16 * jt + l16, i0 = 16 * rt + 4 * lg;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const op_t uh = from_f32<op_t>(u[m]);
+          sUT[jv * LDC + i0 + m] = uh;
+          if constexpr (BF16) sUT2[jv * LDC + i0 + m] = from_f32<op_t>(u[m] - to_f32(uh));
+        }
       }
     }
     __syncthreads();
