@@ -9,6 +9,8 @@ namespace kda {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Log-decay floor: each step keeps at least exp(-5) ~ 0.67% of a key channel
@@ -23,6 +25,18 @@ __device__ __forceinline__ float clamp_log_decay(float g) {
 
 // 2^x on the hardware transcendental unit.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ f32x2 exp2_hw2(f32x2 x) { return f32x2{exp2_hw(x.x), exp2_hw(x.y)}; }
+
+// Two adjacent elements in one register: a bfloat16 pair (low half = lower
+// address) or a float32 pair.  pack2 rounds to nearest even.
+__device__ __forceinline__ uint32_t pack2(f32x2 x, uint32_t*) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+__device__ __forceinline__ f32x2 pack2(f32x2 x, f32x2*) { return x; }
+__device__ __forceinline__ f32x2 unpack2(uint32_t u) {
+  return f32x2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x2 unpack2(f32x2 x) { return x; }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }

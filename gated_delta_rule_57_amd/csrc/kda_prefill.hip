@@ -127,9 +127,12 @@ struct PrefillLayout {
   static constexpr int O_VT = O_P + kC * LDA * 4;
   static constexpr int O_ST = O_VT + DVS * LDC * OPB;
   static constexpr int O_SM = O_ST + DVS * LDK * OPB;
-  // small float32 arrays: beta[64], tau[4][DK], pair[6][DK], egam[DK]
-  static constexpr int SM_BETA = 0, SM_TAU = 64, SM_PAIR = 64 + 4 * DK, SM_EGAM = 64 + 10 * DK;
-  static constexpr int SZ_SM = (64 + 11 * DK) * 4;
+  // small float32 arrays: beta[64], range totals [NRNG][DK], pair[6][DK], egam[DK]
+  // (the scan runs one thread per channel pair and range of a 512-thread group)
+  static constexpr int NRNG = 2 * 512 / DK;
+  static constexpr int SM_BETA = 0, SM_RNG = 64, SM_PAIR = 64 + NRNG * DK;
+  static constexpr int SM_EGAM = SM_PAIR + 6 * DK;
+  static constexpr int SZ_SM = (SM_EGAM + DK) * 4;
   static constexpr int TOTAL = O_SM + SZ_SM;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
@@ -149,15 +152,17 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   constexpr int NJW = NJT / 2;           // value-column tiles per wave (two waves per row tile)
   constexpr int NST = (DK / 16) * NJT;   // state tiles
   constexpr int SPW = NST / NW;          // state tiles per wave
-  constexpr int NH = (NT / DK) < 4 ? NT / DK : 4;  // threads per channel (channel-major phases)
-  constexpr int NCM = NH * DK;           // active channel-major threads
-  constexpr int RPC = kC / NH;           // tokens per channel-major thread
-  constexpr int SPT = RPC / kSub;        // sub-tiles per channel-major thread
+  // channel-major phases: one thread per (channel pair, range of RL tokens)
+  constexpr int NCP = DK / 2;            // channel pairs
+  constexpr int NR = NT / NCP;           // token ranges
+  constexpr int RL = kC / NR;            // tokens per range
+  constexpr int RPS = kSub / RL;         // ranges per sub-tile
+  static_assert(NR == Lay::NRNG && NR * NCP == NT && RL * NR == kC && RPS * RL == kSub, "ranges");
   constexpr int E16 = 16 / sizeof(TIn);  // input elements per 16-byte load
   constexpr int NPF = kC * DK / E16 / NT;
   constexpr int NVT = DVS * (kC / 8);    // v loaders: one value column x 8 tokens each
   static_assert(NPF * E16 * NT == kC * DK && NVT <= NT, "load layout");
-  static_assert(SPW * NW == NST && NJW >= 1 && SPT >= 1 && NCM <= NT, "layout");
+  static_assert(SPW * NW == NST && NJW >= 1, "layout");
 
   extern __shared__ __align__(16) unsigned char smem[];
   op_t* sK = reinterpret_cast<op_t*>(smem + Lay::O_K);
@@ -181,7 +186,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   op_t* sST = reinterpret_cast<op_t*>(smem + Lay::O_ST);
   float* sm = reinterpret_cast<float*>(smem + Lay::O_SM);
   float* sBeta = sm + Lay::SM_BETA;
-  float* sTau = sm + Lay::SM_TAU;
+  float* sRng = sm + Lay::SM_RNG;
   float* sPair = sm + Lay::SM_PAIR;
   float* sEGam = sm + Lay::SM_EGAM;
 
@@ -359,90 +364,99 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     // are unconditional.
     const int64_t tn = (n + 1 < nchunks) ? t0 + kC : t0;
     prefetch(tn, 0);
-    // ---- sub-tile cumulative log-decay: one thread per (channel, token range)
-    const int cc = tid % DK, hh = tid / DK, r0 = RPC * hh;
-    const bool cm = tid < NCM;  // this thread takes part in the channel-major phases
-    float Lr[RPC];  // gamma of each token of this thread
+    // ---- sub-tile cumulative log-decay: one thread per (channel pair, token range);
+    // the ranges' totals go to shared memory for the sub-tile offsets
+    const int cp = tid % NCP, hr = tid / NCP, c0 = 2 * cp, r0 = RL * hr;
+    f32x2 Lr[RL];  // gamma of both channels, per token of this range
+    {
+      f32x2 acc = {0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < SPT && cm; ++s) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < kSub; ++j) {
-        const float gm = sL[(r0 + kSub * s + j) * LDF + cc];
+      for (int j = 0; j < RL; ++j) {
+        const f32x2 gm = *reinterpret_cast<const f32x2*>(sL + (r0 + j) * LDF + c0);
         acc += gm;
-        Lr[kSub * s + j] = gm;
+        Lr[j] = gm;
       }
-      sTau[(r0 / kSub + s) * DK + cc] = acc;
+      *reinterpret_cast<f32x2*>(sRng + hr * DK + c0) = acc;
     }
     __syncthreads();
 
     prefetch(tn, 1);
-    // ---- operands (same thread, same elements, so the updates are in place)
-    typedef op_t vec8 __attribute__((ext_vector_type(8)));
-    vec8 dKc[RPC / 8], dQc[RPC / 8], dKb[RPC / 8];
-    if (cm) {
-      float tau[kNSub];
+    // ---- operands (same thread, same elements, so the updates are in place); two
+    // channels at a time: packed conversions, 32-bit shared-memory accesses
+    typedef typename std::conditional<BF16, uint32_t, f32x2>::type op2_t;
+    auto ld2 = [](const op_t* p) { return *reinterpret_cast<const op2_t*>(p); };
+    auto st2 = [](op_t* p, op2_t x) { *reinterpret_cast<op2_t*>(p) = x; };
+    op2_t dKc[RL], dQc[RL], dKb[RL];
+    {
+      const int R = hr / RPS, part = hr % RPS;
+      f32x2 tau[kNSub], off = {0.f, 0.f};
 #pragma unroll
-      for (int R = 0; R < kNSub; ++R) tau[R] = sTau[R * DK + cc];
-      if (hh == 0) {
-        sPair[0 * DK + cc] = exp2_hw(tau[0]);                    // (1,0)
-        sPair[1 * DK + cc] = exp2_hw(tau[0] + tau[1]);           // (2,0)
-        sPair[2 * DK + cc] = exp2_hw(tau[1]);                    // (2,1)
-        sPair[3 * DK + cc] = exp2_hw(tau[0] + tau[1] + tau[2]);  // (3,0)
-        sPair[4 * DK + cc] = exp2_hw(tau[1] + tau[2]);           // (3,1)
-        sPair[5 * DK + cc] = exp2_hw(tau[2]);                    // (3,2)
-        sEGam[cc] = exp2_hw(tau[0] + tau[1] + tau[2] + tau[3]);
+      for (int J = 0; J < kNSub; ++J) {
+        tau[J] = f32x2{0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < RPS; ++u)
+          tau[J] += *reinterpret_cast<const f32x2*>(sRng + (J * RPS + u) * DK + c0);
       }
 #pragma unroll
-      for (int s = 0; s < SPT; ++s) {
-        const int R = r0 / kSub + s;
-        float ref = 0.f, suf = 0.f;
+      for (int u = 0; u + 1 < RPS; ++u) {  // earlier ranges of this sub-tile
+        const f32x2 t = *reinterpret_cast<const f32x2*>(sRng + (R * RPS + u) * DK + c0);
+        if (u < part) off += t;
+      }
+      const f32x2 own = *reinterpret_cast<const f32x2*>(sRng + hr * DK + c0);
+      if (hr == 0) {
+        *reinterpret_cast<f32x2*>(sPair + 0 * DK + c0) = exp2_hw2(tau[0]);                    // (1,0)
+        *reinterpret_cast<f32x2*>(sPair + 1 * DK + c0) = exp2_hw2(tau[0] + tau[1]);           // (2,0)
+        *reinterpret_cast<f32x2*>(sPair + 2 * DK + c0) = exp2_hw2(tau[1]);                    // (2,1)
+        *reinterpret_cast<f32x2*>(sPair + 3 * DK + c0) = exp2_hw2(tau[0] + tau[1] + tau[2]);  // (3,0)
+        *reinterpret_cast<f32x2*>(sPair + 4 * DK + c0) = exp2_hw2(tau[1] + tau[2]);           // (3,1)
+        *reinterpret_cast<f32x2*>(sPair + 5 * DK + c0) = exp2_hw2(tau[2]);                    // (3,2)
+        *reinterpret_cast<f32x2*>(sEGam + c0) = exp2_hw2(tau[0] + tau[1] + tau[2] + tau[3]);
+      }
+      f32x2 ref = {0.f, 0.f}, suf = {0.f, 0.f};
 #pragma unroll
-        for (int J = 0; J < kNSub; ++J) {
-          if (J < R) ref += tau[J];
-          if (J >= R) suf += tau[J];
+      for (int J = 0; J < kNSub; ++J) {
+        if (J < R) ref += tau[J];
+        else suf += tau[J];
+      }
+      const f32x2 eref = exp2_hw2(ref), ebar = exp2_hw2(suf);
+      // 2^L_j (L = inclusive sub-tile sum) and 2^-L_j as prefix / suffix products of
+      // 2^gamma over the range, started from the range's offset inside its sub-tile
+      f32x2 ep[RL], em[RL];
+      {
+        f32x2 f[RL];
+#pragma unroll
+        for (int j = 0; j < RL; ++j) f[j] = exp2_hw2(Lr[j]);
+        f32x2 pre = exp2_hw2(off), sp = exp2_hw2(-(off + own));
+#pragma unroll
+        for (int j = 0; j < RL; ++j) {
+          pre *= f[j];
+          ep[j] = pre;
         }
-        const float eref = exp2_hw(ref), ebar = exp2_hw(suf);
-        // 2^L_j (L = inclusive sub-tile sum) and 2^-L_j as prefix / suffix products of
-        // 2^gamma: one exp2 per token instead of two.
-        float ep_[kSub], em_[kSub];
-        {
-          float f[kSub];
 #pragma unroll
-          for (int j = 0; j < kSub; ++j) f[j] = exp2_hw(Lr[kSub * s + j]);
-          float pre = 1.f, suf_p = exp2_hw(-tau[R]);
-#pragma unroll
-          for (int j = 0; j < kSub; ++j) {
-            pre *= f[j];
-            ep_[j] = pre;
-          }
-#pragma unroll
-          for (int j = kSub - 1; j >= 0; --j) {
-            em_[j] = suf_p;
-            suf_p *= f[j];
-          }
+        for (int j = RL - 1; j >= 0; --j) {
+          em[j] = sp;
+          sp *= f[j];
         }
+      }
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) {
-          const int r = r0 + kSub * s + j, e = kSub * s + j;
-          const float kf = to_f32(sK[r * LDK + cc]), qf = to_f32(sQ[r * LDK + cc]);
-          const float ep = ep_[j], em = em_[j];
-          const float kr = kf * ep, qr = qf * ep, kd = kf * em;
-          sK[r * LDK + cc] = from_f32<op_t>(kr);
-          const op_t qh = from_f32<op_t>(qr);
-          sQ[r * LDK + cc] = qh;
-          if constexpr (BF16) sQ2[r * LDK + cc] = from_f32<op_t>(qr - to_f32(qh));
-          if constexpr (BF16) {
-            const op_t kh = from_f32<op_t>(kd);
-            sKdH[r * LDK + cc] = kh;
-            sKdL[r * LDK + cc] = from_f32<op_t>(kd - to_f32(kh));
-          } else {
-            sL[r * LDF + cc] = kd;
-          }
-          dKc[e / 8][e % 8] = from_f32<op_t>(kr * eref);
-          dQc[e / 8][e % 8] = from_f32<op_t>(qr * eref);
-          dKb[e / 8][e % 8] = from_f32<op_t>(kd * ebar);
+      for (int j = 0; j < RL; ++j) {
+        const int r = r0 + j;
+        const f32x2 kf = unpack2(ld2(sK + r * LDK + c0)), qf = unpack2(ld2(sQ + r * LDK + c0));
+        const f32x2 kr = kf * ep[j], qr = qf * ep[j], kd = kf * em[j];
+        st2(sK + r * LDK + c0, pack2(kr, (op2_t*)nullptr));
+        const op2_t qh = pack2(qr, (op2_t*)nullptr);
+        st2(sQ + r * LDK + c0, qh);
+        if constexpr (BF16) {
+          st2(sQ2 + r * LDK + c0, pack2(qr - unpack2(qh), (op2_t*)nullptr));
+          const op2_t kh = pack2(kd, (op2_t*)nullptr);
+          st2(sKdH + r * LDK + c0, kh);
+          st2(sKdL + r * LDK + c0, pack2(kd - unpack2(kh), (op2_t*)nullptr));
+        } else {
+          *reinterpret_cast<f32x2*>(sL + r * LDF + c0) = kd;
         }
+        dKc[j] = pack2(kr * eref, (op2_t*)nullptr);
+        dQc[j] = pack2(qr * eref, (op2_t*)nullptr);
+        dKb[j] = pack2(kd * ebar, (op2_t*)nullptr);
       }
     }
     __syncthreads();
@@ -543,21 +557,33 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 
     prefetch(tn, 3);
     // ---- deferred operands into the released region (channel-major threads):
-    // k 2^(G_end - G) transposed (token-contiguous), k 2^G and q 2^G row-major.
+    // k 2^(G_end - G) transposed (token-contiguous: one piece per channel), k 2^G and
+    // q 2^G row-major.
+    if constexpr (BF16) {
+      uint32_t w0[RL / 2], w1[RL / 2];  // bf16 pairs of tokens, channel c0 / c0 + 1
 #pragma unroll
-    for (int e = 0; e < RPC && cm; e += 8) {
-      const vec8 vb = dKb[e / 8];
-      if constexpr (BF16) {
-        *reinterpret_cast<vec8*>(sKbT + cc * LDC + r0 + e) = vb;
-      } else {
-        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e) = f32x4{vb[0], vb[1], vb[2], vb[3]};
-        *reinterpret_cast<f32x4*>(sKbT + cc * LDC + r0 + e + 4) = f32x4{vb[4], vb[5], vb[6], vb[7]};
+      for (int i = 0; i < RL / 2; ++i) {
+        w0[i] = (dKb[2 * i] & 0xffffu) | (dKb[2 * i + 1] << 16);
+        w1[i] = (dKb[2 * i] >> 16) | (dKb[2 * i + 1] & 0xffff0000u);
       }
+      if constexpr (RL == 8) {
+        *reinterpret_cast<uint4*>(sKbT + c0 * LDC + r0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        *reinterpret_cast<uint4*>(sKbT + (c0 + 1) * LDC + r0) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      } else {
+        static_assert(RL == 4, "range length");
+        *reinterpret_cast<uint2*>(sKbT + c0 * LDC + r0) = make_uint2(w0[0], w0[1]);
+        *reinterpret_cast<uint2*>(sKbT + (c0 + 1) * LDC + r0) = make_uint2(w1[0], w1[1]);
+      }
+    } else {
+      static_assert(BF16 || RL == 4, "range length");
+      *reinterpret_cast<f32x4*>(sKbT + c0 * LDC + r0) = f32x4{dKb[0].x, dKb[1].x, dKb[2].x, dKb[3].x};
+      *reinterpret_cast<f32x4*>(sKbT + (c0 + 1) * LDC + r0) =
+          f32x4{dKb[0].y, dKb[1].y, dKb[2].y, dKb[3].y};
     }
 #pragma unroll
-    for (int e = 0; e < RPC && cm; ++e) {
-      sKc[(r0 + e) * LDK + cc] = dKc[e / 8][e % 8];
-      sQc[(r0 + e) * LDK + cc] = dQc[e / 8][e % 8];
+    for (int j = 0; j < RL; ++j) {
+      st2(sKc + (r0 + j) * LDK + c0, dKc[j]);
+      st2(sQc + (r0 + j) * LDK + c0, dQc[j]);
     }
     {  // T' is lower triangular; clear its upper tiles (0,1) and (2,3) (the ones read)
       constexpr int EPP = 16 / Lay::OPB;        // elements per 16-byte piece
