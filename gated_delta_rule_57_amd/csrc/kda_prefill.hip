@@ -105,27 +105,31 @@ struct PrefillLayout {
                                                                          : kC * LDF * 4;
   static constexpr int SZ_KBT = DK * LDC * OPB;
   static constexpr int SZ_QC = kC * LDK * OPB;
-  static constexpr int SZ_TF = kC * LDA * 4;
-  static constexpr int SZ_TB = kC * LDC * OPB;
-  static constexpr int SZ_UT = (BF16 ? 2 : 1) * DVS * LDC * OPB;
+  // Z^T (float32, [value column][token]) and then, in the same rows, U^T: hi part at
+  // element 0, lo part at element ULO (bfloat16); row stride LDZ floats (304 bytes:
+  // 16-byte aligned rows, no bank conflicts across 16 rows)
+  static constexpr int LDZ = kC + 12;
+  static constexpr int LDU = LDZ * 4 / OPB;  // the same rows in operand elements
+  static constexpr int ULO = LDC;
+  static_assert(!BF16 || ULO + kC <= LDU, "U^T hi and lo share a row");
+  static constexpr int SZ_ZU = DVS * LDZ * 4;
+  static constexpr int LDD = 16 + 4;  // diagonal blocks of (I + A)^-1, float32 [64][LDD]
+  static constexpr int SZ_D = kC * LDD * 4;
   static constexpr int PH1 = 2 * SZ_K + SZ_Q2 + SZ_L;
-  static constexpr int PH2 = 2 * SZ_QC + SZ_KBT + SZ_TB + SZ_TF;
+  static constexpr int PH2 = 2 * SZ_QC + SZ_KBT + SZ_ZU + SZ_D;
   static constexpr int REGION = PH1 > PH2 ? PH1 : PH2;
   // phase-1 view of the shared region: raw inputs, then the A/P operands
   static constexpr int O_K = 0, O_Q = SZ_K, O_Q2 = 2 * SZ_K, O_L = 2 * SZ_K + SZ_Q2;
-  // phase-2 view: T float32 last, so that U^T can take its place (and the slack)
-  static constexpr int O_KC = 0, O_TB = SZ_QC, O_QC = O_TB + SZ_TB, O_KBT = O_QC + SZ_QC;
-  static constexpr int O_TF = O_KBT + SZ_KBT;
-  static constexpr int O_UT = O_TF;
-  static_assert(O_UT + SZ_UT <= REGION, "U^T must fit over T and the slack");
+  // phase-2 view: the state-pass operands
+  static constexpr int O_KC = 0, O_QC = SZ_QC, O_KBT = 2 * SZ_QC, O_ZU = O_KBT + SZ_KBT;
+  static constexpr int O_D = O_ZU + SZ_ZU;
   // buffers outside the region
-  // A (float32), then Z^T (hi + lo for bfloat16), then the output staging
-  static constexpr int SZ_ZT = (BF16 ? 2 : 1) * DVS * LDC * OPB;
-  static constexpr int SZ_AW = (kC * LDA * 4 > SZ_ZT) ? kC * LDA * 4 : SZ_ZT;
-  static constexpr int O_A = REGION;  // A, then W
+  static constexpr int SZ_AW = kC * LDA * 4;  // A (float32), then the output staging
+  static constexpr int O_A = REGION;
   static constexpr int O_P = O_A + SZ_AW;
-  static constexpr int O_VT = O_P + kC * LDA * 4;
-  static constexpr int O_ST = O_VT + DVS * LDC * OPB;
+  static constexpr int LDV = DVS + PAD;  // v slice, token-major [64][LDV]
+  static constexpr int O_V = O_P + kC * LDA * 4;
+  static constexpr int O_ST = O_V + kC * LDV * OPB;
   static constexpr int O_SM = O_ST + DVS * LDK * OPB;
   // small float32 arrays: beta[64], range totals [NRNG][DK], pair[6][DK], egam[DK]
   // (the scan runs one thread per channel pair and range of a 512-thread group)
@@ -160,8 +164,9 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   static_assert(NR == Lay::NRNG && NR * NCP == NT && RL * NR == kC && RPS * RL == kSub, "ranges");
   constexpr int E16 = 16 / sizeof(TIn);  // input elements per 16-byte load
   constexpr int NPF = kC * DK / E16 / NT;
-  constexpr int NVT = DVS * (kC / 8);    // v loaders: one value column x 8 tokens each
-  static_assert(NPF * E16 * NT == kC * DK && NVT <= NT, "load layout");
+  constexpr int PPV = DVS / E16;         // 16-byte pieces per token of the v slice
+  constexpr int NPV = (kC * PPV + NT - 1) / NT;  // v pieces per thread (rounded up)
+  static_assert(NPF * E16 * NT == kC * DK && PPV * E16 == DVS, "load layout");
   static_assert(SPW * NW == NST && NJW >= 1, "layout");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -172,17 +177,17 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   op_t* sKdH = reinterpret_cast<op_t*>(smem + Lay::O_L);  // k 2^-L, hi part (bfloat16 inputs)
   op_t* sKdL = sKdH + kC * LDK;                            // lo part
   op_t* sKc = reinterpret_cast<op_t*>(smem + Lay::O_KC);
-  op_t* sTb = reinterpret_cast<op_t*>(smem + Lay::O_TB);
   op_t* sQc = reinterpret_cast<op_t*>(smem + Lay::O_QC);
   op_t* sKbT = reinterpret_cast<op_t*>(smem + Lay::O_KBT);
-  float* sTf = reinterpret_cast<float*>(smem + Lay::O_TF);
-  op_t* sUT = reinterpret_cast<op_t*>(smem + Lay::O_UT);
-  op_t* sUT2 = sUT + DVS * LDC;  // lo part (bf16 only)
+  float* sZT = reinterpret_cast<float*>(smem + Lay::O_ZU);
+  op_t* sUT = reinterpret_cast<op_t*>(smem + Lay::O_ZU);
+  op_t* sUT2 = sUT + Lay::ULO;  // lo part (bf16 only)
+  float* sD = reinterpret_cast<float*>(smem + Lay::O_D);
+  constexpr int LDZ = Lay::LDZ, LDU = Lay::LDU, LDD = Lay::LDD;
   float* sA = reinterpret_cast<float*>(smem + Lay::O_A);
-  op_t* sZT = reinterpret_cast<op_t*>(smem + Lay::O_A);
-  op_t* sZT2 = sZT + DVS * LDC;  // lo part (bf16 only)
   float* sP = reinterpret_cast<float*>(smem + Lay::O_P);
-  op_t* sVT = reinterpret_cast<op_t*>(smem + Lay::O_VT);
+  op_t* sV = reinterpret_cast<op_t*>(smem + Lay::O_V);
+  constexpr int LDV = Lay::LDV;
   op_t* sST = reinterpret_cast<op_t*>(smem + Lay::O_ST);
   float* sm = reinterpret_cast<float*>(smem + Lay::O_SM);
   float* sBeta = sm + Lay::SM_BETA;
@@ -270,10 +275,9 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // ---- register prefetch of one chunk of raw inputs (16-byte pieces).  Addresses
   // are a uniform 64-bit chunk base plus 32-bit per-thread offsets.
   float4 pk[NPF], pq[NPF], pg[NPF];
-  // 8 consecutive tokens of one value column, raw bits in 32-bit containers (no
-  // packing at load time, which would wait for the loads)
-  typedef typename std::conditional<sizeof(TIn) == 2, uint16_t, uint32_t>::type raw_t;
-  uint32_t pv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // stays zero for transition workgroups
+  float4 pv[NPV];  // stays zero for transition workgroups
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) pv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   TIn pbeta = from_f32<TIn>(0.f);  // kept raw: converting here would wait for the load
   // token strides (elements); offsets inside one chunk fit in 32 bits
   const uint32_t rs_k = (uint32_t)(H * DK), rs_v = (uint32_t)(H * DV), rs_b = (uint32_t)H;
@@ -286,12 +290,13 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     const int last = (int)((te - t0) < kC ? (te - t0) : kC) - 1;
     if (part == 0) {
       const TIn* vb = gv + cb * DV + j0;
-      if (tid < NVT && !pmode) {
-        const int jv = tid % DVS, r0v = 8 * (tid / DVS);
+      if (!pmode) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = r0v + e < last ? r0v + e : last;
-          pv[e] = ld_at<raw_t>(vb, ((uint32_t)r * rs_v + (uint32_t)jv) * (uint32_t)sizeof(TIn));
+        for (int i = 0; i < NPV; ++i) {
+          const int pc = tid + NT * i;
+          const int r = min(pc / PPV, last), c = (pc % PPV) * E16;
+          if (pc < kC * PPV)
+            pv[i] = ld_at<float4>(vb, ((uint32_t)r * rs_v + (uint32_t)c) * (uint32_t)sizeof(TIn));
         }
       }
       return;
@@ -334,19 +339,12 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         *reinterpret_cast<f32x4*>(sL + r * LDF + c) = f32x4{gf[0], gf[1], gf[2], gf[3]};
       }
     }
-    if (tid < NVT) {
-      const int jv = tid % DVS, r0v = 8 * (tid / DVS);
-      uint32_t w[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = (r0v + e < nvalid) ? pv[e] : 0u;
-      op_t* dst = sVT + jv * LDC + r0v;
-      if constexpr (BF16) {
-        *reinterpret_cast<uint4*>(dst) =
-            make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
-      } else {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-        *reinterpret_cast<uint4*>(dst + 4) = make_uint4(w[4], w[5], w[6], w[7]);
-      }
+    for (int i = 0; i < NPV; ++i) {
+      const int pc = tid + NT * i;
+      const int r = pc / PPV, c = (pc % PPV) * E16;
+      if (pc < kC * PPV)
+        *reinterpret_cast<uint4*>(sV + r * LDV + c) = mask4(pv[i], r < nvalid ? 0xffffffffu : 0u);
     }
     if (tid < kC) sBeta[tid] = (tid < nvalid) ? to_f32(pbeta) : 0.f;
   };
@@ -474,6 +472,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       const float* pair = sPair + (R * (R - 1) / 2 + I) * DK;  // used off the diagonal only
       f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
       const int row = kSub * R + l16, col = kSub * I + l16;
+      // beta of this lane's four result rows, read before the tile's stores (one read)
+      const f32x4 brow = *reinterpret_cast<const f32x4*>(sBeta + kSub * R + 4 * lg);
 #pragma unroll
       for (int kk = 0; kk < DK; kk += KS) {
         const int k0 = kk + kofs;
@@ -509,10 +509,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = kSub * R + 4 * lg + m, i = col;
-        sA[r * LDA + i] = (!DIAG || i < r) ? sBeta[r] * accA[m] : 0.f;
+        sA[r * LDA + i] = (!DIAG || i < r) ? brow[m] * accA[m] : 0.f;
         sP[r * LDA + i] = (!DIAG || i <= r) ? accP[m] : 0.f;
       }
-      return accA;
+      return DIAG ? accA * brow : accA;  // diagonal: beta-scaled A rows
     };
     if (wave < 4) {
       // (1,0) (3,1) | (2,0) (3,2) | (2,1) | (3,0)
@@ -529,7 +529,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = 4 * lg + m;
-        Nd[m] = (l16 < r) ? sBeta[kSub * R + r] * acc[m] : 0.f;
+        Nd[m] = (l16 < r) ? acc[m] : 0.f;  // acc is already beta-scaled
         Id[m] = (r == l16) ? 1.f : 0.f;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -585,84 +585,19 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       st2(sKc + (r0 + j) * LDK + c0, dKc[j]);
       st2(sQc + (r0 + j) * LDK + c0, dQc[j]);
     }
-    {  // T' is lower triangular; clear its upper tiles (0,1) and (2,3) (the ones read)
-      constexpr int EPP = 16 / Lay::OPB;        // elements per 16-byte piece
-      constexpr int PPR = kSub / EPP;           // pieces per tile row
-      if (tid < 2 * kSub * PPR) {
-        const int u = tid / (kSub * PPR), w = tid % (kSub * PPR);
-        const int r = 32 * u + w / PPR, i = 32 * u + kSub + EPP * (w % PPR);
-        *reinterpret_cast<uint4*>(sTb + r * LDC + i) = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-
-    // ---- T = (I + A)^-1: the diagonal blocks computed with the A tiles go to shared
-    // memory now (float32 for the substitution below, times beta for T' = T Diag(beta))
+    // ---- diagonal blocks D_R = (I + A_RR)^-1, computed with the A tiles, to shared
+    // memory (float32) for the substitution below
     if (wave >= 4) {
       const int R = wave - 4;
-      const float bcol = sBeta[kSub * R + l16];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = kSub * R + 4 * lg + m;
-        sTf[r * LDA + kSub * R + l16] = Dinv[m];
-        sTb[r * LDC + kSub * R + l16] = from_f32<op_t>(Dinv[m] * bcol);
-      }
-    }
-    __syncthreads();
-    // Off-diagonal blocks, all six at once (wave w < 6 takes one):
-    //   T_RI = -D_R sum_{J=I}^{R-1} A_RJ T_JI,
-    // each wave recomputing in registers the lower blocks T_JI its block needs.
-    // Products Z = X Y take X from shared memory (read transposed, as the MFMA
-    // A operand) and Y either from shared memory or from registers (result layout).
-    if (wave < 6) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      auto mul_lr = [&](const float* X, int rx, int cx, const f32x4& Y, f32x4 acc) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          acc = mma_f32(X[(rx + l16) * LDA + cx + 4 * lg + kb], Y[kb], acc);
-        return acc;
-      };
-      auto mul_ll = [&](const float* X, int rx, int cx, const float* Y, int ry, int cy, f32x4 acc) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          acc = mma_f32(X[(rx + l16) * LDA + cx + 4 * lg + kb], Y[(ry + 4 * lg + kb) * LDA + cy + l16], acc);
-        return acc;
-      };
-      // A_RI D_I (the diagonal blocks D_I are in sTf)
-      auto a_d = [&](int R, int I, f32x4 acc) { return mul_ll(sA, kSub * R, kSub * I, sTf, kSub * I, kSub * I, acc); };
-      // -D_R Y
-      auto neg_d = [&](int R, const f32x4& Y) { return -mul_lr(sTf, kSub * R, kSub * R, Y, z); };
-      // A_RJ Y
-      auto a_r = [&](int R, int J, const f32x4& Y, f32x4 acc) { return mul_lr(sA, kSub * R, kSub * J, Y, acc); };
-      int R, I;
-      f32x4 t;
-      if (wave < 3) {  // (1,0) (2,1) (3,2)
-        I = wave;
-        R = wave + 1;
-        t = neg_d(R, a_d(R, I, z));
-      } else if (wave < 5) {  // (2,0) (3,1)
-        I = wave - 3;
-        R = wave - 1;
-        const f32x4 tl = neg_d(I + 1, a_d(I + 1, I, z));  // T_{I+1,I}
-        t = neg_d(R, a_r(R, I + 1, tl, a_d(R, I, z)));
-      } else {  // (3,0)
-        I = 0;
-        R = 3;
-        const f32x4 t10 = neg_d(1, a_d(1, 0, z));
-        const f32x4 t20 = neg_d(2, a_r(2, 1, t10, a_d(2, 0, z)));
-        t = neg_d(3, a_r(3, 2, t20, a_r(3, 1, t10, a_d(3, 0, z))));
-      }
-      const float bcol = sBeta[kSub * I + l16];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        sTb[(kSub * R + 4 * lg + m) * LDC + kSub * I + l16] = from_f32<op_t>(t[m] * bcol);
+      for (int m = 0; m < 4; ++m) sD[(kSub * R + 4 * lg + m) * LDD + l16] = Dinv[m];
     }
     __syncthreads();
 
-    // ---- per row tile, over the key channels: Y = Kc S and Qc S; Z = V - Y.  Then
-    // U = T' Z (= T' V - (T' Kc) S, the correction of the delta rule), which needs Z
-    // of the earlier row tiles: one barrier between.
+    // ---- per row tile, over the key channels: Y = Kc S and Qc S; Z = V - Y, stored
+    // transposed and times beta (float32) for the substitution
     constexpr int NKT = kC / KS;  // k-steps over the chunk's tokens
-    const int kend = 16 * rt + 16;  // T' and P rows of this tile vanish beyond kend
+    const int kend = 16 * rt + 16;  // P rows of this tile vanish beyond kend
     f32x4 Oacc[NJW];
     TOut* sO = reinterpret_cast<TOut*>(smem + Lay::O_A);  // [64][LDO] output staging
     constexpr int LDO = DVS + 16 / (int)sizeof(TOut);
@@ -686,43 +621,73 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         }
       }
       const int i0 = 16 * rt + 4 * lg;
+      const f32x4 brow = *reinterpret_cast<const f32x4*>(sBeta + i0);
 #pragma unroll
       for (int j = 0; j < NJW; ++j) {
         const int jv = 16 * (jt0 + j) + l16;
+        f32x4 z;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float z = to_f32(sVT[jv * LDC + i0 + m]) - y[j][m];
-          const op_t zh = from_f32<op_t>(z);
-          sZT[jv * LDC + i0 + m] = zh;
-          if constexpr (BF16) sZT2[jv * LDC + i0 + m] = from_f32<op_t>(z - to_f32(zh));
-        }
+        for (int m = 0; m < 4; ++m) z[m] = brow[m] * (to_f32(sV[(i0 + m) * LDV + jv]) - y[j][m]);
+        *reinterpret_cast<f32x4*>(sZT + jv * LDZ + i0) = z;
       }
     }
     __syncthreads();
-    {
-      frag aT[NKT];
+
+    // ---- U = (I + A)^-1 Diag(beta) Z by block forward substitution over the four
+    // row tiles, U_R = D_R (beta Z_R - sum_{J<R} A_RJ U_J): one wave per value-column
+    // tile, all in float32 MFMA from registers (no triangular factor is formed).
+    // Each wave reads its whole column tile of Z before writing U over it.
+    if (wave < NJT) {
+      const int jt = wave, jv = 16 * jt + l16;
+      auto mul_lr = [&](const float* X, int ldx, int rx, int cx, const f32x4& Y, f32x4 acc) {
 #pragma unroll
-      for (int q = 0; q < NKT; ++q)
-        if (q * KS < kend) aT[q] = M::ld(sTb + (16 * rt + l16) * LDC + q * KS + kofs);
+        for (int kb = 0; kb < 4; ++kb) acc = mma_f32(X[(rx + l16) * ldx + cx + 4 * lg + kb], Y[kb], acc);
+        return acc;
+      };
+      f32x4 acc[kNSub];  // beta Z_R, then minus the terms of the row tiles already solved
 #pragma unroll
-      for (int j = 0; j < NJW; ++j) {
-        const int jt = jt0 + j;
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+      for (int R = 0; R < kNSub; ++R) acc[R] = *reinterpret_cast<const f32x4*>(sZT + jv * LDZ + kSub * R + 4 * lg);
+      // U (operand type) overwrites Z (float) in these rows: keep every Z load ahead of
+      // the stores (the wave's shared-memory accesses then execute in program order)
+      asm volatile("" ::: "memory");
+      // right-looking: once U_J is known its term goes into every later row tile, so
+      // the chain through the four tiles is one product per step
 #pragma unroll
-        for (int q = 0; q < NKT; ++q) {
-          if (q * KS < kend) {
-            u = M::mma(aT[q], M::ld(sZT + (16 * jt + l16) * LDC + q * KS + kofs), u);
-            if constexpr (BF16) u = M::mma(aT[q], M::ld(sZT2 + (16 * jt + l16) * LDC + q * KS + kofs), u);
-          }
-        }
-        const int jv = 16 * jt + l16, i0 = 16 * rt + 4 * lg;
+      for (int J = 0; J < kNSub; ++J) {
+        const f32x4 u = mul_lr(sD, LDD, kSub * J, 0, acc[J], f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 nu = -u;
+#pragma unroll
+        for (int R = J + 1; R < kNSub; ++R) acc[R] = mul_lr(sA, LDA, kSub * R, kSub * J, nu, acc[R]);
+        const int i0 = kSub * J + 4 * lg;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const op_t uh = from_f32<op_t>(u[m]);
-          sUT[jv * LDC + i0 + m] = uh;
-          if constexpr (BF16) sUT2[jv * LDC + i0 + m] = from_f32<op_t>(u[m] - to_f32(uh));
+          sUT[jv * LDU + i0 + m] = uh;
+          if constexpr (BF16) sUT2[jv * LDU + i0 + m] = from_f32<op_t>(u[m] - to_f32(uh));
         }
       }
+    } else if (BF16 && wave >= 4) {
+      // meanwhile: P (float32) -> hi / lo bfloat16 operand rows in place (hi at element
+      // 0 of the row, lo at element kC); a wave owns whole rows, four lanes per row, so
+      // a row's loads all precede its stores
+      const int r = 16 * (wave - 4) + (lane >> 2), c = 16 * (lane & 3);
+      float pf[16];
+      load8(sP + r * LDA + c, pf);
+      load8(sP + r * LDA + c + 8, pf + 8);
+      typedef typename Mfma<true>::frag bfrag;
+      bfrag h[2], l[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const __bf16 hh_ = (__bf16)pf[e];
+        h[e / 8][e % 8] = hh_;
+        l[e / 8][e % 8] = (__bf16)(pf[e] - (float)hh_);
+      }
+      asm volatile("" ::: "memory");
+      __bf16* row = reinterpret_cast<__bf16*>(sP + r * LDA);
+      *reinterpret_cast<bfrag*>(row + c) = h[0];
+      *reinterpret_cast<bfrag*>(row + c + 8) = h[1];
+      *reinterpret_cast<bfrag*>(row + kC + c) = l[0];
+      *reinterpret_cast<bfrag*>(row + kC + c + 8) = l[1];
     }
     __syncthreads();
 
@@ -734,14 +699,9 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         if (q * KS < kend) {
           const int k0 = q * KS + kofs;
           if constexpr (BF16) {
-            float pf[8];
-            load8(sP + (16 * rt + l16) * LDA + k0, pf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const __bf16 hh_ = (__bf16)pf[e];
-              ph[q][e] = hh_;
-              pl[q][e] = (__bf16)(pf[e] - (float)hh_);
-            }
+            const op_t* row = reinterpret_cast<const op_t*>(sP + (16 * rt + l16) * LDA);
+            ph[q] = M::ld(row + k0);
+            pl[q] = M::ld(row + kC + k0);
           } else {
             ph[q] = sP[(16 * rt + l16) * LDA + k0];
           }
@@ -755,10 +715,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         for (int q = 0; q < NKT; ++q) {
           if (q * KS < kend) {
             const int k0 = q * KS + kofs;
-            const frag uh = M::ld(sUT + (16 * jt + l16) * LDC + k0);
+            const frag uh = M::ld(sUT + (16 * jt + l16) * LDU + k0);
             acc = M::mma(ph[q], uh, acc);
             if constexpr (BF16) {
-              const frag ul = M::ld(sUT2 + (16 * jt + l16) * LDC + k0);
+              const frag ul = M::ld(sUT2 + (16 * jt + l16) * LDU + k0);
               acc = M::mma(pl[q], uh, acc);
               acc = M::mma(ph[q], ul, acc);
             }
@@ -776,36 +736,37 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       frag ak[NKT];
 #pragma unroll
       for (int q = 0; q < NKT; ++q) ak[q] = M::ld(sKbT + (16 * ct + l16) * LDC + q * KS + kofs);
-      f32x4 gam;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) gam[m] = sEGam[16 * ct + 4 * lg + m];
+      const f32x4 gam = *reinterpret_cast<const f32x4*>(sEGam + 16 * ct + 4 * lg);
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
         const int jt = (SPW * wave + i) % NJT;
         f32x4 s = Sacc[i] * gam;
 #pragma unroll
         for (int q = 0; q < NKT; ++q) {
-          s = M::mma(ak[q], M::ld(sUT + (16 * jt + l16) * LDC + q * KS + kofs), s);
-          if constexpr (BF16) s = M::mma(ak[q], M::ld(sUT2 + (16 * jt + l16) * LDC + q * KS + kofs), s);
+          s = M::mma(ak[q], M::ld(sUT + (16 * jt + l16) * LDU + q * KS + kofs), s);
+          if constexpr (BF16) s = M::mma(ak[q], M::ld(sUT2 + (16 * jt + l16) * LDU + q * KS + kofs), s);
         }
         Sacc[i] = s;
       }
     }
     store_state_operand();  // only the row-tile phase reads it, and that phase is over
     __syncthreads();
-    stage(tn);
     if (emit) {  // output: one 16-byte store per piece, rows of DVS contiguous values
       constexpr int PPR = DVS * (int)sizeof(TOut) / 16;  // 16-byte pieces per row
       const int64_t ob = ((b * T + t0) * H + h) * DV + j0;
       const int nvalid = (int)((te - t0) < kC ? (te - t0) : kC);
 #pragma unroll
-      for (int pc = tid; pc < kC * PPR; pc += NT) {
+      for (int it = 0; it < (kC * PPR + NT - 1) / NT; ++it) {
+        const int pc = tid + NT * it;
         const int r = pc / PPR, c = (pc % PPR) * (16 / (int)sizeof(TOut));
+        if (pc >= kC * PPR) break;
         if (r < nvalid)
           st_at<uint4>(go + ob, ((uint32_t)r * rs_v + (uint32_t)c) * (uint32_t)sizeof(TOut),
                        *reinterpret_cast<const uint4*>(sO + r * LDO + c));
       }
     }
+
+    stage(tn);
 
     if (emit && p.ck && (t0 + kC) % p.ck_every == 0 && t0 + kC <= te) {
       const int64_t nck = T / p.ck_every, idx = (t0 + kC) / p.ck_every - 1;
