@@ -639,14 +639,26 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     // Each wave reads its whole column tile of Z before writing U over it.
     if (wave < NJT) {
       const int jt = wave, jv = 16 * jt + l16;
-      auto mul_lr = [&](const float* X, int ldx, int rx, int cx, const f32x4& Y, f32x4 acc) {
+      // the left operands, in the transposed result layout: lane holds X[l16][4 lg + kb]
+      auto left = [&](const float* X, int ldx, int rx, int cx) {
+        return *reinterpret_cast<const f32x4*>(X + (rx + l16) * ldx + cx + 4 * lg);
+      };
+      auto mul = [&](const f32x4& Xt, const f32x4& Y, f32x4 acc) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma_f32(X[(rx + l16) * ldx + cx + 4 * lg + kb], Y[kb], acc);
+        for (int kb = 0; kb < 4; ++kb) acc = mma_f32(Xt[kb], Y[kb], acc);
         return acc;
       };
       f32x4 acc[kNSub];  // beta Z_R, then minus the terms of the row tiles already solved
+      f32x4 dl[kNSub], al[6];  // D_R and A_RJ (J < R), loaded before the chain starts
 #pragma unroll
-      for (int R = 0; R < kNSub; ++R) acc[R] = *reinterpret_cast<const f32x4*>(sZT + jv * LDZ + kSub * R + 4 * lg);
+      for (int R = 0; R < kNSub; ++R) {
+        acc[R] = *reinterpret_cast<const f32x4*>(sZT + jv * LDZ + kSub * R + 4 * lg);
+        dl[R] = left(sD, LDD, kSub * R, 0);
+      }
+#pragma unroll
+      for (int R = 1, n = 0; R < kNSub; ++R)
+#pragma unroll
+        for (int J = 0; J < R; ++J, ++n) al[n] = left(sA, LDA, kSub * R, kSub * J);
       // U (operand type) overwrites Z (float) in these rows: keep every Z load ahead of
       // the stores (the wave's shared-memory accesses then execute in program order)
       asm volatile("" ::: "memory");
@@ -654,10 +666,10 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       // the chain through the four tiles is one product per step
 #pragma unroll
       for (int J = 0; J < kNSub; ++J) {
-        const f32x4 u = mul_lr(sD, LDD, kSub * J, 0, acc[J], f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 u = mul(dl[J], acc[J], f32x4{0.f, 0.f, 0.f, 0.f});
         const f32x4 nu = -u;
 #pragma unroll
-        for (int R = J + 1; R < kNSub; ++R) acc[R] = mul_lr(sA, LDA, kSub * R, kSub * J, nu, acc[R]);
+        for (int R = J + 1; R < kNSub; ++R) acc[R] = mul(al[R * (R - 1) / 2 + J], nu, acc[R]);
         const int i0 = kSub * J + 4 * lg;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
