@@ -38,6 +38,16 @@ def decode_bytes(N, H, dk, dv, in_bytes=2, out_bytes=2) -> float:
     return N * H * per_head
 
 
+def verify_bytes(N, K, H, dk, dv, in_bytes=2, out_bytes=2) -> float:
+    """State read once; K draft tokens' q, k, g, v, beta read; K outputs written."""
+    return N * H * (dk * dv * 4 + K * ((3 * dk + dv + 1) * in_bytes + dv * out_bytes))
+
+
+def commit_bytes(N, K, H, dk, dv, in_bytes=2) -> float:
+    """State read and written once; K tokens' k, g, v, beta read (all accepted)."""
+    return N * H * (2 * dk * dv * 4 + K * ((2 * dk + dv + 1) * in_bytes))
+
+
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_prefill.hip"),
     "decode": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
@@ -132,6 +142,38 @@ def time_decode(kda, torch, w, steps, warmup):
     return us
 
 
+def time_speculative(kda, torch, w, K, reps):
+    """One verify of K draft tokens per sequence and one commit of all of them, timed apart
+    with HIP events on the current stream (mean over `reps` launches of each)."""
+    import synth
+
+    d = synth.device_prefill_inputs(w.replace(T=K), "cuda")  # [N, K, H, .] draft inputs
+    state = d["s0"].clone()
+    o = torch.empty((w.B, K, w.H, w.dv), dtype=d["q"].dtype, device="cuda")
+    accept = torch.full((w.B,), K, dtype=torch.int32, device="cuda")
+
+    def verify():
+        kda.kda_recurrent_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=o)
+
+    def commit():
+        kda.kda_recurrent_commit(d["k"], d["v"], d["g"], d["beta"], accept, state)
+
+    out = {}
+    for name, fn in (("verify", verify), ("commit", commit)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1000.0 / reps
+    assert bool(torch.isfinite(state).all()), "non-finite state after commits"
+    return out
+
+
 def cpu_baseline(w, sample_batches: int):
     """The float64 oracle on the first `sample_batches` sequences of the workload (all heads)."""
     import oracle
@@ -157,6 +199,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--draft", type=int, default=4, help="draft tokens per speculative verify")
     ap.add_argument("--cpu-sample-batches", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -217,6 +260,22 @@ def main():
                                        "traffic": measured_traffic("decode"),
                                        "kernel": "decode_step_kernel<bf16,bf16,128,128>",
                                        "algorithmic_bytes_per_launch": db}}
+        K = args.draft
+        us = time_speculative(kda, torch, wd, K, 200)
+        vb, cb = verify_bytes(wd.B, K, wd.H, wd.dk, wd.dv), commit_bytes(wd.B, K, wd.H, wd.dk, wd.dv)
+        vgbs, cgbs = vb / (us["verify"] * 1e-6) / 1e9, cb / (us["commit"] * 1e-6) / 1e9
+        line["speculative"] = {
+            "workload": f"draft_bf16_n{wd.B}_h{wd.H}_d{wd.dk}_k{K}",
+            "us_per_verify": us["verify"], "us_per_commit": us["commit"],
+            "draft_tokens_per_s": wd.B * K / (us["verify"] * 1e-6),
+            "verify_roofline": {"bound": "hbm", "achieved": vgbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": vgbs / HBM_PEAK_GBS,
+                                "kernel": "multi_token_kernel<bf16,bf16,128,128,verify>",
+                                "algorithmic_bytes_per_launch": vb},
+            "commit_roofline": {"bound": "hbm", "achieved": cgbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": cgbs / HBM_PEAK_GBS,
+                                "kernel": "multi_token_kernel<bf16,bf16,128,128,commit>",
+                                "algorithmic_bytes_per_launch": cb}}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_batches)
     print(json.dumps(line), flush=True)

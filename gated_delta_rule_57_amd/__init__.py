@@ -21,7 +21,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTY
           -4: "KDA_ERR_ALIGN", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_ALIAS", -7: "KDA_ERR_HIP"}
 EXPORTS = ("kda_status_str", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_bytes",
-           "kda_chunk_fwd_segment_tokens", "kda_recurrent_step")
+           "kda_chunk_fwd_segment_tokens", "kda_recurrent_step", "kda_recurrent_verify",
+           "kda_recurrent_commit")
 
 _lib = None
 
@@ -59,6 +60,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_recurrent_step.restype = c_int
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, c_int, c_int, c_int,
                                        c_int, vp]
+    lib.kda_recurrent_verify.restype = c_int
+    lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int,
+                                         c_int, c_int, vp]
+    lib.kda_recurrent_commit.restype = c_int
+    lib.kda_recurrent_commit.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int, c_int,
+                                         vp]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -172,3 +179,36 @@ def kda_recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, o=None, strea
     if st != 0:
         raise KdaError(st, "kda_recurrent_step")
     return o
+
+
+def kda_recurrent_verify(q, k, v, g, beta, state, *, out_dtype=None, o=None, stream=None):
+    """Outputs of K draft tokens per sequence from the committed ``state`` (only read).
+
+    q, k, g [N,K,H,dk]; v [N,K,H,dv]; beta [N,K,H]; state [N,H,dk,dv] float32.
+    Returns o [N,K,H,dv]."""
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    out_dt = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=out_dt, device=q.device)
+    st = load_library().kda_recurrent_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                             _ptr(state), _ptr(o), N, K, H, dk, dv,
+                                             _dtype_code(q.dtype), _dtype_code(o.dtype),
+                                             _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_verify")
+    return o
+
+
+def kda_recurrent_commit(k, v, g, beta, accept, state, *, stream=None):
+    """Advance ``state`` [N,H,dk,dv] in place by accept[n] (int32, on the GPU) draft tokens."""
+    N, K, H, dk = k.shape
+    dv = v.shape[-1]
+    if accept.dtype != torch.int32:
+        raise TypeError("accept must be int32")
+    st = load_library().kda_recurrent_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(accept),
+                                             _ptr(state), N, K, H, dk, dv, _dtype_code(k.dtype),
+                                             _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_recurrent_commit")
+    return state

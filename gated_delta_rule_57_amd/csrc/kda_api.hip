@@ -273,3 +273,58 @@ extern "C" kda_status_t kda_recurrent_step(const void* q, const void* k, const v
                                         out == KDA_BF16, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+namespace {
+
+kda_status_t multi_token_impl(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, const int32_t* accept, float* state, void* o,
+                              int64_t N, int64_t K, int64_t H, int dk, int dv, kda_dtype_t in,
+                              kda_dtype_t out, bool commit, void* stream) {
+  if (!k || !v || !g || !beta || !state) return KDA_ERR_NULL;
+  if (commit ? !accept : (!q || !o)) return KDA_ERR_NULL;
+  if (!dtype_ok(in) || !dtype_ok(out)) return KDA_ERR_DTYPE;
+  if (commit && in != out) return KDA_ERR_DTYPE;  // commit reads no q and writes no o
+  if (N < 1 || K < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_SHAPE;
+  if (!mul_ok(N, H) || N * H > INT32_MAX || !mul_ok(N * H, K) || !mul_ok(N * H * K, 128))
+    return KDA_ERR_SHAPE;
+  const void* ptrs[] = {q, k, v, g, beta, accept, state, o};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const int64_t nh = N * H, ntok = nh * K, es = esize(in);
+  const Span ss = span(state, nh * dk * dv * 4);
+  const Span inputs[] = {span(k, ntok * dk * es), span(v, ntok * dv * es), span(g, ntok * dk * es),
+                         span(beta, ntok * es)};
+  for (const Span& s : inputs)
+    if (overlaps(ss, s)) return KDA_ERR_ALIAS;
+  if (q && overlaps(ss, span(q, ntok * dk * es))) return KDA_ERR_ALIAS;
+  if (commit && overlaps(ss, span(accept, N * 4))) return KDA_ERR_ALIAS;
+  if (!commit) {
+    const Span so = span(o, ntok * dv * esize(out));
+    if (overlaps(so, ss) || overlaps(so, span(q, ntok * dk * es))) return KDA_ERR_ALIAS;
+    for (const Span& s : inputs)
+      if (overlaps(so, s)) return KDA_ERR_ALIAS;
+  }
+  const hipError_t e = kda::multi_token(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv,
+                                        in == KDA_BF16, out == KDA_BF16, commit,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v,
+                                             const void* g, const void* beta, const float* state,
+                                             void* o, int64_t N, int64_t K, int64_t H, int dk,
+                                             int dv, kda_dtype_t in, kda_dtype_t out,
+                                             void* stream) {
+  return multi_token_impl(q, k, v, g, beta, nullptr, const_cast<float*>(state), o, N, K, H, dk,
+                          dv, in, out, false, stream);
+}
+
+extern "C" kda_status_t kda_recurrent_commit(const void* k, const void* v, const void* g,
+                                             const void* beta, const int32_t* accept,
+                                             float* state, int64_t N, int64_t K, int64_t H,
+                                             int dk, int dv, kda_dtype_t in, void* stream) {
+  return multi_token_impl(nullptr, k, v, g, beta, accept, state, nullptr, N, K, H, dk, dv, in, in,
+                          true, stream);
+}

@@ -113,6 +113,135 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
   }
 }
 
+// Speculative decoding: K draft tokens per sequence, inputs [N, K, H, .].
+//   VERIFY: o for every draft token from the committed state; the state is read only.
+//   COMMIT: the state of sequence n advanced in place by accept[n] tokens (clamped
+//           to [0, K]); q and o unused.
+// The draft tokens' projected inputs are all that is kept; the state of an
+// accepted prefix is rebuilt on chip from them (the orkas.ai blog "Kimi K3
+// architecture", section "The cost is paid in the serving stack", describes
+// this in place of rolling back an in-place update).
+//
+// One workgroup per (sequence, head) keeps the state slice in registers (as the
+// single-token kernel does) across the tokens.  The inputs of up to KB tokens are
+// loaded into shared memory at once (with the decays and k.q computed there), so
+// the token loop has no global loads and two barriers per token.
+template <typename TIn, typename TOut, int DK, int DV, bool COMMIT>
+__global__ void __launch_bounds__(256) multi_token_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const TIn* __restrict__ g, const TIn* __restrict__ beta, const int32_t* __restrict__ accept,
+    float* __restrict__ state, TOut* __restrict__ o, int64_t N, int64_t K, int64_t H) {
+  constexpr int NT = 256, KB = 8;
+  constexpr int CG = DV / 4, RG = NT / CG, RPT = DK / RG;
+  static_assert(RPT * RG == DK && CG * RG == NT, "thread layout");
+  constexpr bool WANT_O = !COMMIT;
+  const int64_t hd = blockIdx.x;  // n * H + h
+  if (hd >= N * H) return;
+  const int64_t n = hd / H, h = hd % H;
+  int64_t steps = K;
+  if (COMMIT) {
+    const int64_t a = accept[n];
+    steps = a < 0 ? 0 : (a > K ? K : a);
+    if (steps == 0) return;
+  }
+  const int t = threadIdx.x, cg = t % CG, rg = t / CG;
+  __shared__ float s_q[WANT_O ? KB : 1][DK], s_k[KB][DK], s_dec[KB][DK], s_v[KB][DV];
+  __shared__ float s_beta[KB], s_kq[KB];
+  __shared__ float s_part_a[RG][DV], s_part_b[WANT_O ? RG : 1][DV];
+  __shared__ float s_u[DV];
+
+  float4* st = reinterpret_cast<float4*>(state + hd * (int64_t)(DK * DV));
+  float4 S[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) S[i] = st[(rg + RG * i) * CG + cg];
+
+  for (int64_t j0 = 0; j0 < steps; j0 += KB) {
+    const int nb = (int)((steps - j0) < KB ? (steps - j0) : KB);
+    if (j0 > 0) __syncthreads();  // the previous block is done with the inputs
+    // this block's inputs: token j of the draft is [n, j, h]
+    for (int e = t; e < nb * DK; e += NT) {
+      const int j = e / DK, c = e % DK;
+      const int64_t off = ((n * K + j0 + j) * H + h) * DK + c;
+      if (WANT_O) s_q[j][c] = to_f32(q[off]);
+      s_k[j][c] = to_f32(k[off]);
+      s_dec[j][c] = exp2_hw(clamp_log_decay(to_f32(g[off])) * kLog2e);
+    }
+    for (int e = t; e < nb * DV; e += NT) {
+      const int j = e / DV, c = e % DV;
+      s_v[j][c] = to_f32(v[((n * K + j0 + j) * H + h) * DV + c]);
+    }
+    if (t < nb) s_beta[t] = to_f32(beta[(n * K + j0 + t) * H + h]);
+    __syncthreads();
+    if (WANT_O) {  // k . q of each token: wave w takes tokens w, w + 4
+      const int w = t >> 6, l = t & 63;
+      for (int j = w; j < nb; j += NT / 64) {
+        float x = 0.f;
+#pragma unroll
+        for (int c = l; c < DK; c += 64) x += s_q[j][c] * s_k[j][c];
+        x = wave_sum(x);
+        if (l == 0) s_kq[j] = x;
+      }
+    }
+
+    for (int j = 0; j < nb; ++j) {
+      float4 pa = {0.f, 0.f, 0.f, 0.f}, pb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int c = rg + RG * i;
+        const float d = s_dec[j][c], kc = s_k[j][c];
+        S[i].x *= d;
+        S[i].y *= d;
+        S[i].z *= d;
+        S[i].w *= d;
+        pa.x += kc * S[i].x;
+        pa.y += kc * S[i].y;
+        pa.z += kc * S[i].z;
+        pa.w += kc * S[i].w;
+        if (WANT_O) {
+          const float qc = s_q[j][c];
+          pb.x += qc * S[i].x;
+          pb.y += qc * S[i].y;
+          pb.z += qc * S[i].z;
+          pb.w += qc * S[i].w;
+        }
+      }
+      *reinterpret_cast<float4*>(&s_part_a[rg][4 * cg]) = pa;
+      if (WANT_O) *reinterpret_cast<float4*>(&s_part_b[rg][4 * cg]) = pb;
+      __syncthreads();
+      if (t < DV) {
+        float a = 0.f, bsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          a += s_part_a[r][t];
+          if (WANT_O) bsum += s_part_b[r][t];
+        }
+        const float u = s_beta[j] * (s_v[j][t] - a);
+        s_u[t] = u;
+        if (WANT_O) o[((n * K + j0 + j) * H + h) * DV + t] = from_f32<TOut>(bsum + s_kq[j] * u);
+      }
+      __syncthreads();
+      const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float kc = s_k[j][rg + RG * i];
+        S[i].x += kc * u4.x;
+        S[i].y += kc * u4.y;
+        S[i].z += kc * u4.z;
+        S[i].w += kc * u4.w;
+      }
+      // the next token's partial sums overwrite s_part_* only after everyone has
+      // read them (they were read before the barrier above); s_u is rewritten after
+      // the next token's first barrier, by which time this update is done
+    }
+  }
+  if (COMMIT) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      __builtin_nontemporal_store(f32x4{S[i].x, S[i].y, S[i].z, S[i].w},
+                                  reinterpret_cast<f32x4*>(&st[(rg + RG * i) * CG + cg]));
+  }
+}
+
 template <typename TIn, typename TOut, int DK, int DV>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int64_t nh,
@@ -131,6 +260,39 @@ hipError_t dispatch_decode_d(const void* q, const void* k, const void* v, const 
   if (dk == 64 && dv == 64) return launch_decode<TIn, TOut, 64, 64>(q, k, v, g, beta, state, o, nh, s);
   if (dk == 64 && dv == 128) return launch_decode<TIn, TOut, 64, 128>(q, k, v, g, beta, state, o, nh, s);
   return launch_decode<TIn, TOut, 128, 64>(q, k, v, g, beta, state, o, nh, s);
+}
+
+template <typename TIn, typename TOut, bool COMMIT>
+hipError_t launch_multi(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const int32_t* accept, float* state, void* o, int64_t N,
+                        int64_t K, int64_t H, int dk, int dv, hipStream_t s) {
+  const dim3 grid((unsigned)(N * H)), block(256);
+#define KDA_MULTI(DK_, DV_)                                                                     \
+  multi_token_kernel<TIn, TOut, DK_, DV_, COMMIT><<<grid, block, 0, s>>>(                       \
+      (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, accept, state, \
+      (TOut*)o, N, K, H)
+  if (dk == 128 && dv == 128) KDA_MULTI(128, 128);
+  else if (dk == 64 && dv == 64) KDA_MULTI(64, 64);
+  else if (dk == 64 && dv == 128) KDA_MULTI(64, 128);
+  else KDA_MULTI(128, 64);
+#undef KDA_MULTI
+  return hipGetLastError();
+}
+
+hipError_t multi_token(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const int32_t* accept, float* state, void* o, int64_t N,
+                       int64_t K, int64_t H, int dk, int dv, bool in_bf16, bool out_bf16,
+                       bool commit, hipStream_t s) {
+  if (commit) {
+    return in_bf16 ? launch_multi<__bf16, __bf16, true>(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv, s)
+                   : launch_multi<float, float, true>(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv, s);
+  }
+  if (in_bf16) {
+    return out_bf16 ? launch_multi<__bf16, __bf16, false>(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv, s)
+                    : launch_multi<__bf16, float, false>(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv, s);
+  }
+  return out_bf16 ? launch_multi<float, __bf16, false>(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv, s)
+                  : launch_multi<float, float, false>(q, k, v, g, beta, accept, state, o, N, K, H, dk, dv, s);
 }
 
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,

@@ -51,6 +51,14 @@ hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool ou
 hipError_t segment_scan(const float* s0, const float* seg_z, const float* seg_p, float* seg_in,
                         int64_t B, int64_t H, int64_t nseg, int dk, int dv, hipStream_t s);
 
+// K draft tokens per sequence ([N, K, H, .] inputs): commit = false writes o for
+// every token and leaves the state; commit = true advances the state in place by
+// accept[n] tokens (clamped to [0, K]) and writes no o.
+hipError_t multi_token(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const int32_t* accept, float* state, void* o, int64_t N,
+                       int64_t K, int64_t H, int dk, int dv, bool in_bf16, bool out_bf16,
+                       bool commit, hipStream_t s);
+
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
                        bool in_bf16, bool out_bf16, hipStream_t s);

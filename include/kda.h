@@ -176,6 +176,46 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, con
                                 const void* beta, float* state, void* o, int64_t N, int64_t H,
                                 int dk, int dv, kda_dtype_t in, kda_dtype_t out, void* stream);
 
+/*
+ * Speculative decoding without rollback.  A draft of K tokens per sequence is
+ * checked against the committed state, and only the accepted prefix is
+ * committed.  The state cannot be rolled back once updated in place, so what is
+ * kept for a draft is its tokens' projected inputs (far smaller than the
+ * state); the accepted prefix is replayed from them on chip.  This is the scheme
+ * the orkas.ai blog "Kimi K3 architecture" names for speculative decoding
+ * (section "The cost is paid in the serving stack").
+ *
+ * Draft tensors are [N, K, H, D] (token-major per sequence, like a prefill of
+ * T = K): q, k, g [N, K, H, dk], v [N, K, H, dv], beta [N, K, H].
+ */
+
+/*
+ * kda_recurrent_verify - outputs of K draft tokens from the committed state.
+ *
+ * o[n, j] = S_j^T q[n, j], with S_j the state after draft tokens 0..j applied to
+ * `state` by the recurrence above; `state` [N, H, dk, dv] float32 is only read.
+ *   o  [N, K, H, dv]  dtype `out`, must not overlap the inputs or the state.
+ * Equal to K calls of kda_recurrent_step on a copy of the state.
+ */
+kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v, const void* g,
+                                  const void* beta, const float* state, void* o, int64_t N,
+                                  int64_t K, int64_t H, int dk, int dv, kda_dtype_t in,
+                                  kda_dtype_t out, void* stream);
+
+/*
+ * kda_recurrent_commit - advance each sequence's state by its accepted prefix.
+ *
+ * For every (n, h) the first accept[n] draft tokens (clamped to [0, K]) are
+ * applied to `state` IN PLACE; sequences with accept[n] <= 0 are untouched.
+ *   accept  [N] int32, DEVICE memory (typically written by the verification step).
+ *   k, g, v, beta as for kda_recurrent_verify (q is not needed; dtype `in`).
+ * kda_recurrent_verify and then kda_recurrent_commit with accept[n] = K equals
+ * K calls of kda_recurrent_step.
+ */
+kda_status_t kda_recurrent_commit(const void* k, const void* v, const void* g, const void* beta,
+                                  const int32_t* accept, float* state, int64_t N, int64_t K,
+                                  int64_t H, int dk, int dv, kda_dtype_t in, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -139,6 +139,37 @@ def test_recurrent_step_rejects_before_launch(lib):
     assert _step(lib, o=o, st=3 * FAKE) == -6  # state overlaps v
 
 
+def test_verify_and_commit_reject_before_launch(lib):
+    def verify(**kw):
+        a = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, st=6 * FAKE,
+                 o=64 * FAKE, N=2, K=4, H=2, dk=128, dv=128, din=kda.KDA_BF16, dout=kda.KDA_BF16)
+        a.update(kw)
+        return lib.kda_recurrent_verify(a["q"], a["k"], a["v"], a["g"], a["beta"], a["st"], a["o"],
+                                        a["N"], a["K"], a["H"], a["dk"], a["dv"], a["din"],
+                                        a["dout"], None)
+
+    def commit(**kw):
+        a = dict(k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, acc=7 * FAKE, st=6 * FAKE,
+                 N=2, K=4, H=2, dk=128, dv=128, din=kda.KDA_BF16)
+        a.update(kw)
+        return lib.kda_recurrent_commit(a["k"], a["v"], a["g"], a["beta"], a["acc"], a["st"],
+                                        a["N"], a["K"], a["H"], a["dk"], a["dv"], a["din"], None)
+
+    assert verify(q=None) == -1
+    assert verify(o=None) == -1
+    assert verify(dout=5) == -3
+    assert verify(K=0) == -2
+    assert verify(dk=32) == -2
+    assert verify(o=64 * FAKE + 8) == -4
+    assert verify(o=6 * FAKE + 64) == -6  # o inside the state
+    assert commit(acc=None) == -1
+    assert commit(st=None) == -1
+    assert commit(din=9) == -3
+    assert commit(N=0) == -2
+    assert commit(acc=7 * FAKE + 4) == -4
+    assert commit(st=3 * FAKE) == -6  # state overlaps v
+
+
 def test_binding_rejects_host_tensors():
     import torch
 

@@ -1,0 +1,120 @@
+"""Speculative decoding: kda_recurrent_verify (outputs of K draft tokens from the committed
+state, which stays untouched) and kda_recurrent_commit (state advanced in place by each
+sequence's accepted prefix), against the float64 oracle and against kda_recurrent_step."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_57_amd as kda
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"f32": 1e-5, "bf16": 3e-3}
+
+
+def _draft(w, K, seed):
+    """K draft tokens per sequence: the workload's laws, [N, K, H, .] layout."""
+    x = synth.prefill_inputs(w.replace(B=w.B, T=K, seed=seed))
+    # a state of the size a long prefill leaves (sigma 0.5 rather than 0.02)
+    s0 = 25.0 * synth.prefill_inputs(w.replace(T=1, seed=seed + 1000, init_state=True))["s0"]
+    return x, s0
+
+
+def _oracle_steps(x, s0, steps):
+    """Oracle outputs of every draft token and the state after steps[n] tokens."""
+    N, K = x["q"].shape[:2]
+    o = np.zeros(x["v"].shape)
+    S = s0.copy()
+    S_acc = s0.copy()
+    for j in range(K):
+        o[:, j], S = oracle.kda_decode_step(S, x["q"][:, j], x["k"][:, j], x["v"][:, j],
+                                            x["g"][:, j], x["beta"][:, j])
+        for n in range(N):
+            if j + 1 == steps[n]:
+                S_acc[n] = S[n]
+    return o, S_acc
+
+
+def _np(t):
+    return t.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("bf16", 128, 128), ("bf16", 64, 128),
+                                         ("bf16", 128, 64), ("f32", 128, 128)])
+def test_verify_and_commit_match_oracle(dtype, dk, dv):
+    N, K, H = 6, 5, 3
+    w = synth.PREFILL_B4_T4096.replace(B=N, H=H, dk=dk, dv=dv, dtype=dtype)
+    x, s0 = _draft(w, K, seed=11)
+    accept = np.array([0, 1, 2, 3, 5, 9], dtype=np.int32)  # 9 > K: clamped to K
+    steps = np.minimum(accept, K)
+    o_r, s_r = _oracle_steps(x, s0, steps)
+    d = synth.to_torch(x, dtype, DEV)
+    state = torch.from_numpy(s0).float().to(DEV)
+    state0 = state.clone()
+    o = kda.kda_recurrent_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], state,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(state, state0)  # verification leaves the state alone
+    acc = torch.from_numpy(accept).to(DEV)
+    kda.kda_recurrent_commit(d["k"], d["v"], d["g"], d["beta"], acc, state)
+    torch.cuda.synchronize()
+    e_o = oracle.rel_l2(_np(o), o_r)
+    e_s = oracle.rel_l2(_np(state), s_r)
+    print(f"[spec] {dtype} dk{dk} dv{dv} N{N} K{K}: o {e_o:.3e} state {e_s:.3e}", flush=True)
+    assert e_o <= TOL[dtype] and e_s <= TOL[dtype]
+    # accept = 0: that sequence's state is bitwise untouched
+    assert torch.equal(state[0], state0[0])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_accept_equals_single_steps(dtype):
+    """verify + commit(K) against K kda_recurrent_step calls."""
+    d_ = 64 if dtype == "f32" else 128
+    N, K, H = 4, 6, 2
+    w = synth.PREFILL_B4_T4096.replace(B=N, H=H, dk=d_, dv=d_, dtype=dtype)
+    x, s0 = _draft(w, K, seed=21)
+    d = synth.to_torch(x, dtype, DEV)
+    state = torch.from_numpy(s0).float().to(DEV)
+    ref = state.clone()
+    o = kda.kda_recurrent_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], state,
+                                 out_dtype=torch.float32)
+    kda.kda_recurrent_commit(d["k"], d["v"], d["g"], d["beta"],
+                             torch.full((N,), K, dtype=torch.int32, device=DEV), state)
+    outs = []
+    for j in range(K):
+        outs.append(kda.kda_recurrent_step(d["q"][:, j].contiguous(), d["k"][:, j].contiguous(),
+                                           d["v"][:, j].contiguous(), d["g"][:, j].contiguous(),
+                                           d["beta"][:, j].contiguous(), ref, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    o_steps = torch.stack(outs, 1)
+    e_o = oracle.rel_l2(_np(o), _np(o_steps))
+    e_s = oracle.rel_l2(_np(state), _np(ref))
+    print(f"[spec] {dtype}: verify vs steps o {e_o:.3e}, commit vs steps state {e_s:.3e}", flush=True)
+    # the same per-token arithmetic; only the compiler's scheduling of two copies differs
+    assert e_o <= 1e-6 and e_s <= 1e-6
+
+
+def test_rejected_draft_then_new_draft():
+    """Reject part of a draft, then verify a fresh draft from the committed prefix: the
+    outputs are those of the accepted tokens followed by the new ones."""
+    N, K, H = 3, 4, 2
+    w = synth.PREFILL_B4_T4096.replace(B=N, H=H)
+    x1, s0 = _draft(w, K, seed=31)
+    x2, _ = _draft(w, K, seed=32)
+    accept = np.array([1, 4, 2], dtype=np.int32)
+    d1, d2 = synth.to_torch(x1, "bf16", DEV), synth.to_torch(x2, "bf16", DEV)
+    state = torch.from_numpy(s0).float().to(DEV)
+    kda.kda_recurrent_verify(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], state)
+    kda.kda_recurrent_commit(d1["k"], d1["v"], d1["g"], d1["beta"],
+                             torch.from_numpy(accept).to(DEV), state)
+    o2 = kda.kda_recurrent_verify(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], state,
+                                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # oracle: per sequence, accepted tokens of draft 1 then all of draft 2
+    _, S1 = _oracle_steps(x1, s0, accept)
+    o_r, _ = _oracle_steps(x2, S1, np.full(N, K))
+    e = oracle.rel_l2(_np(o2), o_r)
+    print(f"[spec] reject then redraft: o {e:.3e}", flush=True)
+    assert e <= 3e-3
