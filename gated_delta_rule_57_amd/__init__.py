@@ -21,8 +21,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTY
           -4: "KDA_ERR_ALIGN", -5: "KDA_ERR_WORKSPACE", -6: "KDA_ERR_ALIAS", -7: "KDA_ERR_HIP"}
 EXPORTS = ("kda_status_str", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_bytes",
-           "kda_chunk_fwd_segment_tokens", "kda_recurrent_step", "kda_recurrent_verify",
-           "kda_recurrent_commit")
+           "kda_chunk_fwd_segment_tokens", "kda_chunk_fwd_checkpoints_at", "kda_recurrent_step",
+           "kda_recurrent_verify", "kda_recurrent_commit")
 
 _lib = None
 
@@ -60,6 +60,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_recurrent_step.restype = c_int
     lib.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, c_int, c_int, c_int,
                                        c_int, vp]
+    lib.kda_chunk_fwd_checkpoints_at.restype = c_int
+    lib.kda_chunk_fwd_checkpoints_at.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
+                                                 i64, i64, c_int, c_int, c_int, c_int, c_int, vp,
+                                                 sz, vp]
     lib.kda_recurrent_verify.restype = c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int,
                                          c_int, c_int, vp]
@@ -212,3 +216,33 @@ def kda_recurrent_commit(k, v, g, beta, accept, state, *, stream=None):
     if st != 0:
         raise KdaError(st, "kda_recurrent_commit")
     return state
+
+
+def kda_chunk_fwd_checkpoints_at(q, k, v, g, beta, positions, initial_state=None, *,
+                                 out_dtype=None, o=None, final_state=None, checkpoints=None,
+                                 chunk: int = 64, workspace=None, stream=None):
+    """Chunked forward saving the state after each of ``positions`` tokens (int64 on the GPU,
+    increasing multiples of ``chunk``).  Returns (o, final_state, checkpoints [B,P,H,dk,dv])."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    P = positions.numel()
+    if positions.dtype != torch.int64:
+        raise TypeError("positions must be int64")
+    out_dt = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dt, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if checkpoints is None:
+        checkpoints = torch.empty((B, P, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, q.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_fwd_checkpoints_at(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+        _ptr(final_state), _ptr(checkpoints), _ptr(positions), P, B, T, H, dk, dv, chunk,
+        _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_checkpoints_at")
+    return o, final_state, checkpoints

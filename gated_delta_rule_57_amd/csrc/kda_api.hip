@@ -116,9 +116,13 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
                             float* final_state, float* checkpoints, int64_t checkpoint_every,
                             int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
                             kda_dtype_t in, kda_dtype_t out, int64_t seg_len, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, const int64_t* ck_pos = nullptr,
+                            int64_t n_ck = 0) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
-  if (checkpoint_every != 0 && !checkpoints) return KDA_ERR_NULL;
+  if ((checkpoint_every != 0 || n_ck != 0) && !checkpoints) return KDA_ERR_NULL;
+  if (n_ck != 0 && !ck_pos) return KDA_ERR_NULL;
+  if (n_ck < 0 || (n_ck > 0 && checkpoint_every != 0)) return KDA_ERR_SHAPE;
+  if (ck_pos && (reinterpret_cast<uintptr_t>(ck_pos) & 7u) != 0) return KDA_ERR_ALIGN;
   if (!dtype_ok(in) || !dtype_ok(out)) return KDA_ERR_DTYPE;
   if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return KDA_ERR_SHAPE;
   if (checkpoint_every < 0 || (checkpoint_every % chunk) != 0) return KDA_ERR_SHAPE;
@@ -157,8 +161,9 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
         overlaps(sf, span(initial_state, state_bytes)))
       return KDA_ERR_ALIAS;
   }
-  if (checkpoints) {
-    const int64_t nck = T / checkpoint_every;
+  const int64_t nck = n_ck > 0 ? n_ck : (checkpoint_every ? T / checkpoint_every : 0);
+  if (!mul_ok(B * H, nck) || !mul_ok(B * H * nck, (int64_t)dk * dv * 4)) return KDA_ERR_SHAPE;
+  if (checkpoints && nck > 0) {
     const Span sc = span(checkpoints, B * nck * H * dk * dv * 4);
     if (overlaps(sc, so)) return KDA_ERR_ALIAS;
     for (const Span& s : inputs)
@@ -173,14 +178,15 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
     if (overlaps(sw, so)) return KDA_ERR_ALIAS;
     if (initial_state && overlaps(sw, span(initial_state, state_bytes))) return KDA_ERR_ALIAS;
     if (final_state && overlaps(sw, span(final_state, state_bytes))) return KDA_ERR_ALIAS;
-    if (checkpoints && overlaps(sw, span(checkpoints, B * (T / checkpoint_every) * H * dk * dv * 4)))
+    if (checkpoints && nck > 0 && overlaps(sw, span(checkpoints, B * nck * H * dk * dv * 4)))
       return KDA_ERR_ALIAS;
   }
 
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, o, final_state,
-                     checkpoint_every ? checkpoints : nullptr, B, T, H, checkpoint_every,
-                     nseg > 1 ? seg_len : T, nseg, 0, nullptr, nullptr, nullptr};
+                     nck > 0 ? checkpoints : nullptr, B, T, H, checkpoint_every,
+                     nseg > 1 ? seg_len : T, nseg, 0, nullptr, nullptr, nullptr,
+                     n_ck > 0 ? ck_pos : nullptr, n_ck};
   if (nseg > 1) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* seg_in = reinterpret_cast<float*>(ws);
@@ -327,4 +333,19 @@ extern "C" kda_status_t kda_recurrent_commit(const void* k, const void* v, const
                                              int dk, int dv, kda_dtype_t in, void* stream) {
   return multi_token_impl(nullptr, k, v, g, beta, accept, state, nullptr, N, K, H, dk, dv, in, in,
                           true, stream);
+}
+
+extern "C" kda_status_t kda_chunk_fwd_checkpoints_at(
+    const void* q, const void* k, const void* v, const void* g, const void* beta,
+    const float* initial_state, void* o, float* final_state, float* checkpoints,
+    const int64_t* positions, int64_t n_positions, int64_t B, int64_t T, int64_t H, int dk, int dv,
+    int chunk, kda_dtype_t in, kda_dtype_t out, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (n_positions < 1) return KDA_ERR_SHAPE;
+  const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          : kChunk;
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints, 0, B, T, H,
+                        dk, dv, chunk, in, out, seg, workspace, workspace_bytes, stream, positions,
+                        n_positions);
 }

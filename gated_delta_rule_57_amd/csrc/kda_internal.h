@@ -33,6 +33,11 @@ struct PrefillArgs {
   const float* seg_in;
   float* seg_z;
   float* seg_p;
+  // checkpoints at listed positions instead of every ck_every tokens: ck_pos
+  // (device, n_ck entries) holds token counts; entry i of ck is the state after
+  // ck_pos[i] tokens, written only if that is a chunk end in (0, T]
+  const int64_t* ck_pos;
+  int64_t n_ck;
 };
 
 // d_v slice width per prefill workgroup.

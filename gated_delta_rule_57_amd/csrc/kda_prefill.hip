@@ -350,6 +350,17 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   };
 
   const int64_t nchunks = (te - tb + kC - 1) / kC;
+  // listed checkpoint positions: the first one past this walk's first chunk
+  int64_t ck_next = 0;
+  if (emit && p.ck && p.ck_pos) {
+    int64_t lo = 0, hi = p.n_ck;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (p.ck_pos[mid] < tb + kC) lo = mid + 1;
+      else hi = mid;
+    }
+    ck_next = lo;
+  }
   for (int part = 0; part < 4; ++part) prefetch(tb, part);
   stage(tb);
   __syncthreads();
@@ -780,9 +791,21 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 
     stage(tn);
 
-    if (emit && p.ck && (t0 + kC) % p.ck_every == 0 && t0 + kC <= te) {
-      const int64_t nck = T / p.ck_every, idx = (t0 + kC) / p.ck_every - 1;
-      float* dst = p.ck + ((b * nck + idx) * H + h) * (int64_t)DK * DV;
+    // checkpoint: every ck_every tokens, or at the listed positions (ck_pos)
+    int64_t ck_idx = -1, nck = 0;
+    if (emit && p.ck) {
+      const int64_t end = t0 + kC;  // tokens consumed after this chunk
+      if (p.ck_pos) {
+        while (ck_next < p.n_ck && p.ck_pos[ck_next] < end) ++ck_next;
+        if (ck_next < p.n_ck && p.ck_pos[ck_next] == end && end <= te) ck_idx = ck_next++;
+        nck = p.n_ck;
+      } else if (end % p.ck_every == 0 && end <= te) {
+        nck = T / p.ck_every;
+        ck_idx = end / p.ck_every - 1;
+      }
+    }
+    if (ck_idx >= 0) {
+      float* dst = p.ck + ((b * nck + ck_idx) * H + h) * (int64_t)DK * DV;
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
         const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;

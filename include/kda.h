@@ -177,6 +177,30 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, con
                                 int dk, int dv, kda_dtype_t in, kda_dtype_t out, void* stream);
 
 /*
+ * kda_chunk_fwd_checkpoints_at - kda_chunk_fwd with states saved at listed positions.
+ *
+ * Same as kda_chunk_fwd (same workspace) with checkpoint_every = 0, except that
+ * checkpoint i is the state after `positions[i]` tokens:
+ *   positions    [n_positions] int64, DEVICE memory, strictly increasing, each a
+ *                multiple of `chunk` in (0, T].  An entry that is not such a
+ *                position leaves its checkpoint untouched (the kernel never
+ *                writes outside the checkpoint array).  8-byte aligned.
+ *   checkpoints  [B, n_positions, H, dk, dv] float32.
+ * This serves prefix caching that hashes fixed token blocks and keeps the
+ * recurrent state only at a sparse subset of block ends (the orkas.ai blog "Kimi
+ * K3 architecture", section "The cost is paid in the serving stack"); a cache hit
+ * restores a checkpoint as `initial_state` of the following call.
+ */
+kda_status_t kda_chunk_fwd_checkpoints_at(const void* q, const void* k, const void* v,
+                                          const void* g, const void* beta,
+                                          const float* initial_state, void* o, float* final_state,
+                                          float* checkpoints, const int64_t* positions,
+                                          int64_t n_positions, int64_t B, int64_t T, int64_t H,
+                                          int dk, int dv, int chunk, kda_dtype_t in,
+                                          kda_dtype_t out, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
  * Speculative decoding without rollback.  A draft of K tokens per sequence is
  * checked against the committed state, and only the accepted prefix is
  * committed.  The state cannot be rolled back once updated in place, so what is

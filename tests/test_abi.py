@@ -170,6 +170,24 @@ def test_verify_and_commit_reject_before_launch(lib):
     assert commit(st=3 * FAKE) == -6  # state overlaps v
 
 
+def test_checkpoints_at_rejects_before_launch(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=2 * FAKE, v=3 * FAKE, g=4 * FAKE, beta=5 * FAKE, o=64 * FAKE,
+                 ck=96 * FAKE, pos=8 * FAKE, n=2, B=1, T=256, H=1, dk=128, dv=128)
+        a.update(kw)
+        return lib.kda_chunk_fwd_checkpoints_at(a["q"], a["k"], a["v"], a["g"], a["beta"], None,
+                                                a["o"], None, a["ck"], a["pos"], a["n"], a["B"],
+                                                a["T"], a["H"], a["dk"], a["dv"], 64, kda.KDA_BF16,
+                                                kda.KDA_BF16, None, 0, None)
+
+    assert call(n=0) == -2
+    assert call(n=-3) == -2
+    assert call(pos=None) == -1
+    assert call(ck=None) == -1
+    assert call(pos=8 * FAKE + 4) == -4
+    assert call(ck=64 * FAKE + 128) == -6  # checkpoints overlap o
+
+
 def test_binding_rejects_host_tensors():
     import torch
 
