@@ -22,7 +22,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTY
 EXPORTS = ("kda_status_str", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_bytes",
            "kda_chunk_fwd_segment_tokens", "kda_chunk_fwd_checkpoints_at", "kda_recurrent_step",
-           "kda_recurrent_verify", "kda_recurrent_commit")
+           "kda_recurrent_verify", "kda_recurrent_commit", "kda_chunk_fwd_gate_logits",
+           "kda_recurrent_step_gate_logits")
 
 _lib = None
 
@@ -64,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_checkpoints_at.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64,
                                                  i64, i64, c_int, c_int, c_int, c_int, c_int, vp,
                                                  sz, vp]
+    lib.kda_chunk_fwd_gate_logits.restype = c_int
+    lib.kda_chunk_fwd_gate_logits.argtypes = list(lib.kda_chunk_fwd.argtypes)
+    lib.kda_recurrent_step_gate_logits.restype = c_int
+    lib.kda_recurrent_step_gate_logits.argtypes = list(lib.kda_recurrent_step.argtypes)
     lib.kda_recurrent_verify.restype = c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int,
                                          c_int, c_int, vp]
@@ -125,7 +130,7 @@ def kda_chunk_fwd_segment_tokens(B: int, T: int, H: int, dk: int, dv: int, chunk
 def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=None,
                   final_state=None, want_final_state=True, checkpoint_every: int = 0,
                   checkpoints=None, chunk: int = 64, workspace=None, stream=None,
-                  segment_tokens: Optional[int] = None):
+                  segment_tokens: Optional[int] = None, gate_logits: bool = False):
     """Chunked KDA forward.  Shapes as in include/kda.h; returns (o, final_state, checkpoints).
 
     q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (all one dtype); initial_state
@@ -133,7 +138,8 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
     final_state=initial_state for an in-place state update.  ``segment_tokens``
     None calls kda_chunk_fwd (the library picks the segmentation); an integer
     calls kda_chunk_fwd_segmented with that segment length.  A workspace of the
-    size the library asks for is allocated when not given.
+    size the library asks for is allocated when not given.  ``gate_logits=True``
+    passes raw decay logits in ``g`` (kda_chunk_fwd_gate_logits; log-decay = -softplus).
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -159,7 +165,11 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
             _ptr(final_state), _ptr(checkpoints), int(checkpoint_every), B, T, H, dk, dv, chunk,
             _dtype_code(in_dt), _dtype_code(o.dtype))
     tail = (_ptr(workspace), ws_bytes, _stream(stream))
-    if segment_tokens is None:
+    if gate_logits:
+        if segment_tokens is not None:
+            raise ValueError("gate_logits takes the library's segmentation")
+        st, where = lib.kda_chunk_fwd_gate_logits(*args, *tail), "kda_chunk_fwd_gate_logits"
+    elif segment_tokens is None:
         st, where = lib.kda_chunk_fwd(*args, *tail), "kda_chunk_fwd"
     else:
         st = lib.kda_chunk_fwd_segmented(*args, int(segment_tokens), *tail)
@@ -169,17 +179,19 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
     return o, final_state, checkpoints
 
 
-def kda_recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, o=None, stream=None):
-    """One decode step; ``state`` [N,H,dk,dv] float32 is updated in place.  Returns o [N,H,dv]."""
+def kda_recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, o=None, stream=None,
+                       gate_logits: bool = False):
+    """One decode step; ``state`` [N,H,dk,dv] float32 is updated in place.  Returns o [N,H,dv].
+    ``gate_logits=True`` passes raw decay logits in ``g``."""
     N, H, dk = q.shape
     dv = v.shape[-1]
     out_dt = q.dtype if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dt, device=q.device)
-    st = load_library().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                           _ptr(state), _ptr(o), N, H, dk, dv,
-                                           _dtype_code(q.dtype), _dtype_code(o.dtype),
-                                           _stream(stream))
+    lib = load_library()
+    fn = lib.kda_recurrent_step_gate_logits if gate_logits else lib.kda_recurrent_step
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, dk, dv,
+            _dtype_code(q.dtype), _dtype_code(o.dtype), _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_recurrent_step")
     return o

@@ -117,7 +117,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
                             int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
                             kda_dtype_t in, kda_dtype_t out, int64_t seg_len, void* workspace,
                             size_t workspace_bytes, void* stream, const int64_t* ck_pos = nullptr,
-                            int64_t n_ck = 0) {
+                            int64_t n_ck = 0, bool gate_logits = false) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
   if ((checkpoint_every != 0 || n_ck != 0) && !checkpoints) return KDA_ERR_NULL;
   if (n_ck != 0 && !ck_pos) return KDA_ERR_NULL;
@@ -186,7 +186,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, o, final_state,
                      nck > 0 ? checkpoints : nullptr, B, T, H, checkpoint_every,
                      nseg > 1 ? seg_len : T, nseg, 0, nullptr, nullptr, nullptr,
-                     n_ck > 0 ? ck_pos : nullptr, n_ck};
+                     n_ck > 0 ? ck_pos : nullptr, n_ck, gate_logits ? 1 : 0};
   if (nseg > 1) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* seg_in = reinterpret_cast<float*>(ws);
@@ -256,10 +256,10 @@ extern "C" kda_status_t kda_chunk_fwd_segmented(
                         workspace, workspace_bytes, stream);
 }
 
-extern "C" kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v,
-                                           const void* g, const void* beta, float* state, void* o,
-                                           int64_t N, int64_t H, int dk, int dv, kda_dtype_t in,
-                                           kda_dtype_t out, void* stream) {
+static kda_status_t recurrent_step_impl(const void* q, const void* k, const void* v, const void* g,
+                                        const void* beta, float* state, void* o, int64_t N,
+                                        int64_t H, int dk, int dv, kda_dtype_t in, kda_dtype_t out,
+                                        void* stream, bool gate_logits) {
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
   if (!dtype_ok(in) || !dtype_ok(out)) return KDA_ERR_DTYPE;
   if (N < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_SHAPE;
@@ -276,8 +276,24 @@ extern "C" kda_status_t kda_recurrent_step(const void* q, const void* k, const v
   for (const Span& s : inputs)
     if (overlaps(so, s) || overlaps(ss, s)) return KDA_ERR_ALIAS;
   const hipError_t e = kda::decode_step(q, k, v, g, beta, state, o, nh, dk, dv, in == KDA_BF16,
-                                        out == KDA_BF16, reinterpret_cast<hipStream_t>(stream));
+                                        out == KDA_BF16, reinterpret_cast<hipStream_t>(stream),
+                                        gate_logits);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v,
+                                           const void* g, const void* beta, float* state, void* o,
+                                           int64_t N, int64_t H, int dk, int dv, kda_dtype_t in,
+                                           kda_dtype_t out, void* stream) {
+  return recurrent_step_impl(q, k, v, g, beta, state, o, N, H, dk, dv, in, out, stream, false);
+}
+
+extern "C" kda_status_t kda_recurrent_step_gate_logits(const void* q, const void* k, const void* v,
+                                                       const void* a, const void* beta,
+                                                       float* state, void* o, int64_t N,
+                                                       int64_t H, int dk, int dv, kda_dtype_t in,
+                                                       kda_dtype_t out, void* stream) {
+  return recurrent_step_impl(q, k, v, a, beta, state, o, N, H, dk, dv, in, out, stream, true);
 }
 
 namespace {
@@ -348,4 +364,17 @@ extern "C" kda_status_t kda_chunk_fwd_checkpoints_at(
   return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints, 0, B, T, H,
                         dk, dv, chunk, in, out, seg, workspace, workspace_bytes, stream, positions,
                         n_positions);
+}
+
+extern "C" kda_status_t kda_chunk_fwd_gate_logits(
+    const void* q, const void* k, const void* v, const void* a, const void* beta,
+    const float* initial_state, void* o, float* final_state, float* checkpoints,
+    int64_t checkpoint_every, int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+    kda_dtype_t in, kda_dtype_t out, void* workspace, size_t workspace_bytes, void* stream) {
+  const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          : kChunk;
+  return chunk_fwd_impl(q, k, v, a, beta, initial_state, o, final_state, checkpoints,
+                        checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
+                        workspace_bytes, stream, nullptr, 0, true);
 }

@@ -18,7 +18,7 @@
 
 namespace kda {
 
-template <typename TIn, typename TOut, int DK, int DV>
+template <typename TIn, typename TOut, int DK, int DV, bool LOGITS>
 __global__ void __launch_bounds__(256) decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ beta, float* __restrict__ state,
@@ -49,7 +49,8 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
     const int64_t off = hd * DK + t;
     s_q[t] = to_f32(q[off]);
     s_k[t] = to_f32(k[off]);
-    s_dec[t] = exp2_hw(clamp_log_decay(to_f32(g[off])) * kLog2e);
+    s_dec[t] = exp2_hw(LOGITS ? gamma_from_logit(to_f32(g[off]))
+                              : clamp_log_decay(to_f32(g[off])) * kLog2e);
   }
   __syncthreads();
   if (t < 64) {
@@ -242,24 +243,32 @@ __global__ void __launch_bounds__(256) multi_token_kernel(
   }
 }
 
-template <typename TIn, typename TOut, int DK, int DV>
+template <typename TIn, typename TOut, int DK, int DV, bool LOGITS>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int64_t nh,
                          hipStream_t stream) {
-  decode_step_kernel<TIn, TOut, DK, DV><<<dim3((unsigned)nh), dim3(256), 0, stream>>>(
+  decode_step_kernel<TIn, TOut, DK, DV, LOGITS><<<dim3((unsigned)nh), dim3(256), 0, stream>>>(
       (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, state,
       (TOut*)o, nh);
   return hipGetLastError();
 }
 
+template <typename TIn, typename TOut, bool LOGITS>
+hipError_t dispatch_decode_dl(const void* q, const void* k, const void* v, const void* g,
+                              const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
+                              hipStream_t s) {
+  if (dk == 128 && dv == 128) return launch_decode<TIn, TOut, 128, 128, LOGITS>(q, k, v, g, beta, state, o, nh, s);
+  if (dk == 64 && dv == 64) return launch_decode<TIn, TOut, 64, 64, LOGITS>(q, k, v, g, beta, state, o, nh, s);
+  if (dk == 64 && dv == 128) return launch_decode<TIn, TOut, 64, 128, LOGITS>(q, k, v, g, beta, state, o, nh, s);
+  return launch_decode<TIn, TOut, 128, 64, LOGITS>(q, k, v, g, beta, state, o, nh, s);
+}
+
 template <typename TIn, typename TOut>
 hipError_t dispatch_decode_d(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                             hipStream_t s) {
-  if (dk == 128 && dv == 128) return launch_decode<TIn, TOut, 128, 128>(q, k, v, g, beta, state, o, nh, s);
-  if (dk == 64 && dv == 64) return launch_decode<TIn, TOut, 64, 64>(q, k, v, g, beta, state, o, nh, s);
-  if (dk == 64 && dv == 128) return launch_decode<TIn, TOut, 64, 128>(q, k, v, g, beta, state, o, nh, s);
-  return launch_decode<TIn, TOut, 128, 64>(q, k, v, g, beta, state, o, nh, s);
+                             hipStream_t s, bool gate_logits) {
+  return gate_logits ? dispatch_decode_dl<TIn, TOut, true>(q, k, v, g, beta, state, o, nh, dk, dv, s)
+                     : dispatch_decode_dl<TIn, TOut, false>(q, k, v, g, beta, state, o, nh, dk, dv, s);
 }
 
 template <typename TIn, typename TOut, bool COMMIT>
@@ -297,13 +306,14 @@ hipError_t multi_token(const void* q, const void* k, const void* v, const void* 
 
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                       bool in_bf16, bool out_bf16, hipStream_t s) {
+                       bool in_bf16, bool out_bf16, hipStream_t s, bool gate_logits) {
+  const bool L = gate_logits;
   if (in_bf16) {
-    return out_bf16 ? dispatch_decode_d<__bf16, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s)
-                    : dispatch_decode_d<__bf16, float>(q, k, v, g, beta, state, o, nh, dk, dv, s);
+    return out_bf16 ? dispatch_decode_d<__bf16, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s, L)
+                    : dispatch_decode_d<__bf16, float>(q, k, v, g, beta, state, o, nh, dk, dv, s, L);
   }
-  return out_bf16 ? dispatch_decode_d<float, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s)
-                  : dispatch_decode_d<float, float>(q, k, v, g, beta, state, o, nh, dk, dv, s);
+  return out_bf16 ? dispatch_decode_d<float, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s, L)
+                  : dispatch_decode_d<float, float>(q, k, v, g, beta, state, o, nh, dk, dv, s, L);
 }
 
 }  // namespace kda

@@ -23,6 +23,17 @@ __device__ __forceinline__ float clamp_log_decay(float g) {
   return (g != g) ? g : fminf(fmaxf(g, kLogDecayFloor), 0.0f);
 }
 
+// Log-decay in base-2 units from a raw decay logit a: clamp(-softplus(a)) * log2(e),
+// with -softplus(a) = -log2(1 + 2^(a log2 e)) / log2(e) (the negative-softplus map of
+// the Towards-AI article on Kimi K3, "Kimi Delta Attention (KDA)").  For a above ~88
+// 2^(...) overflows to +inf and the result is the floor, as it should be; NaN stays
+// NaN.  In float32 1 + 2^t rounds away 2^t < 2^-24, i.e. log-decays above -6e-8
+// become 0 (a relative decay error below 1e-7).
+__device__ __forceinline__ float gamma_from_logit(float a) {
+  const float t = -__builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(a * kLog2e));
+  return (a != a) ? a : fminf(fmaxf(t, kLogDecayFloor * kLog2e), 0.0f);
+}
+
 // 2^x on the hardware transcendental unit.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ f32x2 exp2_hw2(f32x2 x) { return f32x2{exp2_hw(x.x), exp2_hw(x.y)}; }

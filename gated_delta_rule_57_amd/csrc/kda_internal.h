@@ -38,6 +38,8 @@ struct PrefillArgs {
   // ck_pos[i] tokens, written only if that is a chunk end in (0, T]
   const int64_t* ck_pos;
   int64_t n_ck;
+  // g holds raw decay logits a (log-decay = -softplus(a)) instead of log-decays
+  int gate_logits;
 };
 
 // d_v slice width per prefill workgroup.
@@ -66,6 +68,6 @@ hipError_t multi_token(const void* q, const void* k, const void* v, const void* 
 
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                       bool in_bf16, bool out_bf16, hipStream_t s);
+                       bool in_bf16, bool out_bf16, hipStream_t s, bool gate_logits = false);
 
 }  // namespace kda

@@ -330,9 +330,15 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       *reinterpret_cast<uint4*>(sQ + r * LDK + c) = mask4(pq[i], mk);
       float gf[E16];
       unpack16(pg[i], (TIn*)nullptr, gf);
+      if (p.gate_logits) {  // raw decay logits: negative softplus, then the floor
 #pragma unroll
-      for (int e = 0; e < E16; ++e)
-        gf[e] = __uint_as_float(__float_as_uint(clamp_log_decay(gf[e]) * kLog2e) & mk);
+        for (int e = 0; e < E16; ++e)
+          gf[e] = __uint_as_float(__float_as_uint(gamma_from_logit(gf[e])) & mk);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E16; ++e)
+          gf[e] = __uint_as_float(__float_as_uint(clamp_log_decay(gf[e]) * kLog2e) & mk);
+      }
       if constexpr (E16 == 8) {
         store8(sL + r * LDF + c, gf);
       } else {

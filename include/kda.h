@@ -177,6 +177,25 @@ kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v, con
                                 int dk, int dv, kda_dtype_t in, kda_dtype_t out, void* stream);
 
 /*
+ * Raw decay logits.  These variants take, in place of g, the decay logits `a`
+ * (same shape and dtype) and use g = -softplus(a) = -log(1 + e^a) before the
+ * floor: the negative-softplus map of the Towards-AI article on the Kimi K3
+ * report (section "Kimi Delta Attention (KDA)"), fused into the kernels' gate
+ * preparation.  Everything else is as in kda_chunk_fwd / kda_recurrent_step.
+ * In float32, log-decays above about -6e-8 (a < -16.6) round to 0.
+ */
+kda_status_t kda_chunk_fwd_gate_logits(const void* q, const void* k, const void* v, const void* a,
+                                       const void* beta, const float* initial_state, void* o,
+                                       float* final_state, float* checkpoints,
+                                       int64_t checkpoint_every, int64_t B, int64_t T, int64_t H,
+                                       int dk, int dv, int chunk, kda_dtype_t in, kda_dtype_t out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+kda_status_t kda_recurrent_step_gate_logits(const void* q, const void* k, const void* v,
+                                            const void* a, const void* beta, float* state, void* o,
+                                            int64_t N, int64_t H, int dk, int dv, kda_dtype_t in,
+                                            kda_dtype_t out, void* stream);
+
+/*
  * kda_chunk_fwd_checkpoints_at - kda_chunk_fwd with states saved at listed positions.
  *
  * Same as kda_chunk_fwd (same workspace) with checkpoint_every = 0, except that

@@ -33,6 +33,7 @@ composition law of the blog's "The cost is paid in the serving stack"
 section, and hand-derived worked examples under tests/golden/.
 """
 from .kda import (  # noqa: F401
+    log_decay_from_logits,
     LOG_DECAY_FLOOR,
     clamp_log_decay,
     kda_decode_step,

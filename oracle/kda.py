@@ -21,6 +21,15 @@ def clamp_log_decay(g: np.ndarray) -> np.ndarray:
     return np.minimum(np.maximum(np.asarray(g, dtype=np.float64), LOG_DECAY_FLOOR), 0.0)
 
 
+def log_decay_from_logits(a: np.ndarray) -> np.ndarray:
+    """g = -softplus(a) = -log(1 + e^a): the negative-softplus map from decay logits to
+    log-decays (Towards-AI article on the Kimi K3 report, section "Kimi Delta Attention
+    (KDA)").  Computed as -logaddexp(0, a) in float64, which is exact to rounding for
+    every finite a; NaN stays NaN.  The floor is applied afterwards by the recurrence."""
+    with np.errstate(invalid="ignore"):  # NaN in, NaN out
+        return -np.logaddexp(0.0, np.asarray(a, dtype=np.float64))
+
+
 def _step(S, q, k, v, g, beta):
     """One token for a stack of states.
 

@@ -132,8 +132,9 @@ def _draw_block(rng, B, t, H, dk, dv, a_law):
     k = _unit(rng.standard_normal((B, t, H, dk)))
     v = rng.standard_normal((B, t, H, dv))
     beta = _sigmoid(rng.standard_normal((B, t, H)))
-    g = np.maximum(-_softplus(_decay_logits(rng, (B, t, H, dk), a_law)), -5.0)
-    return q, k, v, g, beta
+    a = _decay_logits(rng, (B, t, H, dk), a_law)
+    g = np.maximum(-_softplus(a), -5.0)
+    return q, k, v, g, beta, a
 
 
 def initial_state(w: Workload, heads: Optional[slice] = None) -> np.ndarray:
@@ -147,11 +148,13 @@ def initial_state(w: Workload, heads: Optional[slice] = None) -> np.ndarray:
     return s0 if heads is None else s0[:, heads]
 
 
-def prefill_inputs(w: Workload, t_end: Optional[int] = None):
+def prefill_inputs(w: Workload, t_end: Optional[int] = None, with_logits: bool = False):
     """Inputs of a prefill workload for tokens [0, t_end).
 
     Returns a dict of float64 arrays (exactly the storage-dtype values):
-    q, k [B,t,H,dk]; v [B,t,H,dv]; g [B,t,H,dk]; beta [B,t,H]; s0 [B,H,dk,dv].
+    q, k [B,t,H,dk]; v [B,t,H,dv]; g [B,t,H,dk]; beta [B,t,H]; s0 [B,H,dk,dv];
+    with ``with_logits`` also the raw decay logits a [B,t,H,dk] that g was made
+    from (rounded to the storage dtype on their own).
     """
     assert w.kind == "prefill"
     t_end = w.T if t_end is None else min(t_end, w.T)
@@ -163,7 +166,7 @@ def prefill_inputs(w: Workload, t_end: Optional[int] = None):
         arrs = _draw_block(rng, w.B, tb, w.H, w.dk, w.dv, w.a_law)
         keep = min(tb, t_end - t0)
         parts.append([x[:, :keep] for x in arrs])
-    names = ("q", "k", "v", "g", "beta")
+    names = ("q", "k", "v", "g", "beta") + (("a",) if with_logits else ())
     out = {n: round_to(np.concatenate([p[i] for p in parts], axis=1), w.dtype)
            for i, n in enumerate(names)}
     out["s0"] = initial_state(w)
@@ -178,7 +181,7 @@ def decode_step_inputs(w: Workload, step: int, seqs: Optional[slice] = None):
     assert w.kind == "decode"
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, DECODE_STREAM,
                                                                       step])))
-    q, k, v, g, beta = _draw_block(rng, w.B, 1, w.H, w.dk, w.dv, w.a_law)
+    q, k, v, g, beta, _ = _draw_block(rng, w.B, 1, w.H, w.dk, w.dv, w.a_law)
     out = {}
     for n, x in zip(("q", "k", "v", "g", "beta"), (q, k, v, g, beta)):
         x = x[:, 0]

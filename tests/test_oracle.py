@@ -333,3 +333,26 @@ def test_pins_reject_planted_mistakes(mutant, monkeypatch):
     except (AssertionError, ValueError):
         failures += 1
     assert failures > 0, f"{mutant.__name__} passed every pin"
+
+
+# ------------------------------------------------------------- raw decay logits
+def test_negative_softplus_closed_forms():
+    """Towards-AI article, "Kimi Delta Attention (KDA)": decay logits map to log-decays by
+    negative softplus.  Pinned by closed forms, not by re-evaluating the same formula."""
+    f = oracle.log_decay_from_logits
+    assert f(0.0) == pytest.approx(-np.log(2.0), abs=1e-16)
+    # softplus(log(e - 1)) = log(e) = 1
+    assert f(np.log(np.e - 1.0)) == pytest.approx(-1.0, abs=1e-15)
+    # softplus(log(3)) = log(4)
+    assert f(np.log(3.0)) == pytest.approx(-2.0 * np.log(2.0), abs=1e-15)
+    # tails: softplus(a) = a + e^-a + O(e^-2a) for large a, e^a - e^2a/2 for very negative a
+    assert f(40.0) == pytest.approx(-(40.0 + np.exp(-40.0)), rel=1e-15)
+    assert f(-40.0) == pytest.approx(-np.exp(-40.0), rel=1e-12)
+    assert np.isnan(f(np.nan)) and f(np.inf) == -np.inf and f(-np.inf) == 0.0
+    # the derivative of softplus is the logistic function
+    a, h = np.linspace(-8.0, 8.0, 33), 1e-6
+    assert np.allclose((f(a - h) - f(a + h)) / (2 * h), 1.0 / (1.0 + np.exp(-a)), atol=1e-8)
+    # strictly decreasing and below zero; the -5 floor is reached at a = log(e^5 - 1)
+    g = f(np.linspace(-20.0, 20.0, 401))
+    assert np.all(np.diff(g) < 0) and np.all(g < 0)
+    assert oracle.clamp_log_decay(f(np.log(np.expm1(5.0)))) == pytest.approx(-5.0, abs=1e-14)
