@@ -51,6 +51,8 @@ def commit_bytes(N, K, H, dk, dv, in_bytes=2) -> float:
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_prefill.hip"),
     "decode": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
+    "verify": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
+    "commit": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 COPY_CALIBRATION_BYTES = 1 << 30
@@ -270,10 +272,12 @@ def main():
             "draft_tokens_per_s": wd.B * K / (us["verify"] * 1e-6),
             "verify_roofline": {"bound": "hbm", "achieved": vgbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": vgbs / HBM_PEAK_GBS,
+                                "traffic": measured_traffic("verify"),
                                 "kernel": "multi_token_kernel<bf16,bf16,128,128,verify>",
                                 "algorithmic_bytes_per_launch": vb},
             "commit_roofline": {"bound": "hbm", "achieved": cgbs, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": cgbs / HBM_PEAK_GBS,
+                                "traffic": measured_traffic("commit"),
                                 "kernel": "multi_token_kernel<bf16,bf16,128,128,commit>",
                                 "algorithmic_bytes_per_launch": cb}}
     if not args.no_cpu_baseline:
