@@ -3,16 +3,19 @@
 // MFMA accumulators for the whole sequence.
 //
 // Method (chunk of C = 64 tokens, 16-token sub-tiles R = 0..3; log-decays in
-// base-2 units, gamma = clamp(g) * log2(e)):
+// base-2 units, gamma = clamp(g) * log2(e), e = 2^gamma per token and channel):
 //   L_r    inclusive cumulative gamma inside r's sub-tile;  tau_R its total
 //   ref_R  sum of tau over earlier sub-tiles (chunk-relative start of R)
 //   A[r,i] = beta_r sum_c k_rc k_ic 2^(G_rc - G_ic)     i < r   (G = ref + L)
 //   P[r,i] =        sum_c q_rc k_ic 2^(G_rc - G_ic)     i <= r
-//   T      = (I + A)^-1 Diag(beta)        (UT / WY form of the delta rule)
-//   W      = T (k 2^G),   U0 = T V
-//   U      = U0 - W S                     (S = state entering the chunk)
-//   O      = (q 2^G) S + P U
+//   U      = (I + A)^-1 Diag(beta) (V - Kc S)     (UT form; Kc = k 2^G, S = state
+//            entering the chunk), by block forward substitution over the sub-tiles
+//            with the diagonal blocks D_R = (I + A_RR)^-1
+//   O      = Qc S + P U                   (Qc = q 2^G)
 //   S'     = Diag(2^G_end) S + (k 2^(G_end - G))^T U
+// Every 2^(...) above is a product of the per-token factors e (a prefix or suffix
+// product inside a token range, times range and sub-tile totals), so the only
+// transcendental per element is the one that forms e.
 // A and P are built per 16x16 tile pair (R, I <= R) as one dense MFMA product
 // of a row operand x 2^(L_r) (<= 1) and a column operand x 2^(ref_R - G_i).
 // On off-diagonal tiles the column factor is <= 1; on the diagonal tiles it is
@@ -24,19 +27,21 @@
 // "Kimi Delta Attention (KDA)" section refers to.
 //
 // Precision (bfloat16 inputs): MFMA operands are bfloat16 with float32
-// accumulation.  The output path through P (q 2^L, the column operand, P
-// itself) and U are carried as hi + lo bfloat16 pairs (three products per
-// pair of split operands); A, T, W, (q 2^G), S and the state-update key
-// operand are single bfloat16.  float32 inputs use the float32 MFMA throughout.
+// accumulation.  The output path through the diagonal P tiles (q 2^L and the
+// column operand on those tiles, P itself) and U are carried as hi + lo bfloat16
+// pairs (three products per pair of split operands); A, Kc, Qc, S and the
+// state-update key operand are single bfloat16; the inverses and the block
+// substitution run in float32.  float32 inputs use the float32 MFMA throughout.
 //
-// Schedule of one chunk (eight waves, two per SIMD; wave w owns row tile w%4 of
-// the chunk for half of the value-column tiles, and a fixed set of state
-// tiles; "|" = barrier):
-//   stage prefetched inputs, prefetch the next chunk | sub-tile scans (one
-//   thread per channel and token range) | operands | A and P tile pairs |
-//   diagonal 16x16 inverses, (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8) on MFMA
-//   from registers | three block-substitution levels | per row tile: W, U0,
-//   U = U0 - W S, Qc S | P U, output, state update | state to its MFMA operand.
+// Schedule of one chunk (eight waves, two per SIMD; "|" = barrier):
+//   range decay products (one thread per channel pair and token range) |
+//   operands | A and P tile pairs, the diagonal pairs' waves then invert
+//   I + A_RR on MFMA from registers | deferred operands (Kc, Qc, transposed
+//   state-update keys) | per row tile: Kc S, Qc S, Z = beta (V - Kc S) | block
+//   substitution for U (four waves), P to hi / lo rows (four waves) | P U,
+//   output tile, state update | output stores, next chunk's inputs to shared
+//   memory.
+
 #include <type_traits>
 
 #include "kda_device.h"
@@ -99,7 +104,7 @@ struct PrefillLayout {
 
   static constexpr int SZ_K = kC * LDK * OPB;
   static constexpr int SZ_Q2 = BF16 ? kC * LDK * OPB : 0;
-  // gamma (float32) during the scan; then the column operand k 2^-L, as float32
+  // 2^gamma (float32) for the decay products; then the column operand k 2^-L, as float32
   // (float32 inputs) or as a hi + lo pair of bfloat16 arrays
   static constexpr int SZ_L = (BF16 && 2 * kC * LDK * OPB > kC * LDF * 4) ? 2 * kC * LDK * OPB
                                                                          : kC * LDF * 4;
@@ -242,7 +247,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   const int64_t head_off = (b * H + h) * (int64_t)DK * DV;       // [B, H, DK, DV] states
   const int64_t seg_unit = (b * p.nseg + seg) * H + h;           // [B, nseg, H, ...] states
 
-  // ---- state slice in accumulators: tiles tt = SPW*wave + i -> (ct, jt)
+  // ---- state slice in accumulators: a wave holds one value-column tile jt = wave % NJT
+  // and SPW key-channel tiles ct = (wave / NJT) SPW + i
   const float* src = nullptr;  // entry state (row stride DV), NULL = zeros
   if (emit)
     src = p.nseg > 1 ? p.seg_in + seg_unit * DK * DV : (p.s0 ? p.s0 + head_off : nullptr);
@@ -251,7 +257,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   f32x4 Sacc[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
-    const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
+    const int ct = (wave / NJT) * SPW + i, jt = wave % NJT;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int c = 16 * ct + 4 * lg + m, jv = 16 * jt + l16;
@@ -264,7 +270,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   auto store_state_operand = [&]() {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
+      const int ct = (wave / NJT) * SPW + i, jt = wave % NJT;
       op_t* dst = sST + (16 * jt + l16) * LDK + 16 * ct + 4 * lg;
 #pragma unroll
       for (int m = 0; m < 4; ++m) dst[m] = from_f32<op_t>(Sacc[i][m]);
@@ -314,8 +320,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     if (part == 3 && tid < kC)
       pbeta = ld_at<TIn>(gb + cb, (uint32_t)min(tid, last) * rs_b * (uint32_t)sizeof(TIn));
   };
-  // Prefetched chunk starting at token t0 -> shared memory: k, q raw; g -> gamma
-  // (float32); v^T; beta.  Rows past the end become beta = 0, g = 0, k = q = v = 0
+  // Prefetched chunk starting at token t0 -> shared memory: k, q raw; g -> 2^gamma
+  // (float32); v; beta.  Rows past the end become beta = 0, g = 0, k = q = v = 0
   // tokens, which leave the state unchanged.
   auto stage = [&](int64_t t0) {
     const int nvalid = (int)((te - t0) < kC ? (te - t0) : kC);
@@ -330,15 +336,17 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       *reinterpret_cast<uint4*>(sQ + r * LDK + c) = mask4(pq[i], mk);
       float gf[E16];
       unpack16(pg[i], (TIn*)nullptr, gf);
+      // per-token decay 2^gamma (1 on padded rows)
       if (p.gate_logits) {  // raw decay logits: negative softplus, then the floor
 #pragma unroll
-        for (int e = 0; e < E16; ++e)
-          gf[e] = __uint_as_float(__float_as_uint(gamma_from_logit(gf[e])) & mk);
+        for (int e = 0; e < E16; ++e) gf[e] = exp2_hw(gamma_from_logit(gf[e]));
       } else {
 #pragma unroll
-        for (int e = 0; e < E16; ++e)
-          gf[e] = __uint_as_float(__float_as_uint(clamp_log_decay(gf[e]) * kLog2e) & mk);
+        for (int e = 0; e < E16; ++e) gf[e] = exp2_hw(clamp_log_decay(gf[e]) * kLog2e);
       }
+#pragma unroll
+      for (int e = 0; e < E16; ++e)
+        gf[e] = __uint_as_float((__float_as_uint(gf[e]) & mk) | (0x3f800000u & ~mk));
       if constexpr (E16 == 8) {
         store8(sL + r * LDF + c, gf);
       } else {
@@ -379,18 +387,17 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     // are unconditional.
     const int64_t tn = (n + 1 < nchunks) ? t0 + kC : t0;
     prefetch(tn, 0);
-    // ---- sub-tile cumulative log-decay: one thread per (channel pair, token range);
-    // the ranges' totals go to shared memory for the sub-tile offsets
+    // ---- decay products: one thread per (channel pair, token range); the ranges'
+    // products go to shared memory for the sub-tile offsets
     const int cp = tid % NCP, hr = tid / NCP, c0 = 2 * cp, r0 = RL * hr;
-    f32x2 Lr[RL];  // gamma of both channels, per token of this range
+    f32x2 Lr[RL];  // 2^gamma of both channels, per token of this range
     {
-      f32x2 acc = {0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < RL; ++j) {
-        const f32x2 gm = *reinterpret_cast<const f32x2*>(sL + (r0 + j) * LDF + c0);
-        acc += gm;
-        Lr[j] = gm;
-      }
+      for (int j = 0; j < RL; ++j)
+        Lr[j] = *reinterpret_cast<const f32x2*>(sL + (r0 + j) * LDF + c0);
+      f32x2 acc = Lr[0];
+#pragma unroll
+      for (int j = 1; j < RL; ++j) acc *= Lr[j];
       *reinterpret_cast<f32x2*>(sRng + hr * DK + c0) = acc;
     }
     __syncthreads();
@@ -404,44 +411,47 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     op2_t dKc[RL], dQc[RL], dKb[RL];
     {
       const int R = hr / RPS, part = hr % RPS;
-      f32x2 tau[kNSub], off = {0.f, 0.f};
+      // decay products (2^ of the log-decay sums): tau[J] over sub-tile J, off over the
+      // earlier ranges of this thread's sub-tile, own over its own range
+      f32x2 tau[kNSub], off = {1.f, 1.f};
 #pragma unroll
       for (int J = 0; J < kNSub; ++J) {
-        tau[J] = f32x2{0.f, 0.f};
+        tau[J] = *reinterpret_cast<const f32x2*>(sRng + (J * RPS) * DK + c0);
 #pragma unroll
-        for (int u = 0; u < RPS; ++u)
-          tau[J] += *reinterpret_cast<const f32x2*>(sRng + (J * RPS + u) * DK + c0);
+        for (int u = 1; u < RPS; ++u)
+          tau[J] *= *reinterpret_cast<const f32x2*>(sRng + (J * RPS + u) * DK + c0);
       }
 #pragma unroll
       for (int u = 0; u + 1 < RPS; ++u) {  // earlier ranges of this sub-tile
         const f32x2 t = *reinterpret_cast<const f32x2*>(sRng + (R * RPS + u) * DK + c0);
-        if (u < part) off += t;
+        if (u < part) off *= t;
       }
       const f32x2 own = *reinterpret_cast<const f32x2*>(sRng + hr * DK + c0);
       if (hr == 0) {
-        *reinterpret_cast<f32x2*>(sPair + 0 * DK + c0) = exp2_hw2(tau[0]);                    // (1,0)
-        *reinterpret_cast<f32x2*>(sPair + 1 * DK + c0) = exp2_hw2(tau[0] + tau[1]);           // (2,0)
-        *reinterpret_cast<f32x2*>(sPair + 2 * DK + c0) = exp2_hw2(tau[1]);                    // (2,1)
-        *reinterpret_cast<f32x2*>(sPair + 3 * DK + c0) = exp2_hw2(tau[0] + tau[1] + tau[2]);  // (3,0)
-        *reinterpret_cast<f32x2*>(sPair + 4 * DK + c0) = exp2_hw2(tau[1] + tau[2]);           // (3,1)
-        *reinterpret_cast<f32x2*>(sPair + 5 * DK + c0) = exp2_hw2(tau[2]);                    // (3,2)
-        *reinterpret_cast<f32x2*>(sEGam + c0) = exp2_hw2(tau[0] + tau[1] + tau[2] + tau[3]);
+        const f32x2 t01 = tau[0] * tau[1], t12 = tau[1] * tau[2];
+        *reinterpret_cast<f32x2*>(sPair + 0 * DK + c0) = tau[0];          // (1,0)
+        *reinterpret_cast<f32x2*>(sPair + 1 * DK + c0) = t01;             // (2,0)
+        *reinterpret_cast<f32x2*>(sPair + 2 * DK + c0) = tau[1];          // (2,1)
+        *reinterpret_cast<f32x2*>(sPair + 3 * DK + c0) = t01 * tau[2];    // (3,0)
+        *reinterpret_cast<f32x2*>(sPair + 4 * DK + c0) = t12;             // (3,1)
+        *reinterpret_cast<f32x2*>(sPair + 5 * DK + c0) = tau[2];          // (3,2)
+        *reinterpret_cast<f32x2*>(sEGam + c0) = t01 * (tau[2] * tau[3]);
       }
-      f32x2 ref = {0.f, 0.f}, suf = {0.f, 0.f};
+      f32x2 eref = {1.f, 1.f}, ebar = {1.f, 1.f};  // 2^ref, 2^suf
 #pragma unroll
       for (int J = 0; J < kNSub; ++J) {
-        if (J < R) ref += tau[J];
-        else suf += tau[J];
+        if (J < R) eref *= tau[J];
+        else ebar *= tau[J];
       }
-      const f32x2 eref = exp2_hw2(ref), ebar = exp2_hw2(suf);
       // 2^L_j (L = inclusive sub-tile sum) and 2^-L_j as prefix / suffix products of
       // 2^gamma over the range, started from the range's offset inside its sub-tile
       f32x2 ep[RL], em[RL];
       {
-        f32x2 f[RL];
-#pragma unroll
-        for (int j = 0; j < RL; ++j) f[j] = exp2_hw2(Lr[j]);
-        f32x2 pre = exp2_hw2(off), sp = exp2_hw2(-(off + own));
+        const f32x2* f = Lr;
+        // 2^-L at the range's last token: the reciprocal (to 1 ulp) of its prefix
+        // product; a sub-tile's product stays >= 2^(-16 * 5 log2 e), a normal float
+        const f32x2 po = off * own;
+        f32x2 pre = off, sp = f32x2{__builtin_amdgcn_rcpf(po.x), __builtin_amdgcn_rcpf(po.y)};
 #pragma unroll
         for (int j = 0; j < RL; ++j) {
           pre *= f[j];
@@ -760,20 +770,25 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       }
     }
     {
-      static_assert(NJT % SPW == 0, "a wave's state tiles share one key-channel tile");
-      const int ct = (SPW * wave) / NJT;
-      frag ak[NKT];
+      static_assert(NW % NJT == 0, "whole value-column tiles per wave");
+      // this wave's value-column tile of U, read once for its SPW key-channel tiles
+      const int jt = wave % NJT;
+      frag uh[NKT], ul[NKT];
 #pragma unroll
-      for (int q = 0; q < NKT; ++q) ak[q] = M::ld(sKbT + (16 * ct + l16) * LDC + q * KS + kofs);
-      const f32x4 gam = *reinterpret_cast<const f32x4*>(sEGam + 16 * ct + 4 * lg);
+      for (int q = 0; q < NKT; ++q) {
+        uh[q] = M::ld(sUT + (16 * jt + l16) * LDU + q * KS + kofs);
+        if constexpr (BF16) ul[q] = M::ld(sUT2 + (16 * jt + l16) * LDU + q * KS + kofs);
+      }
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
-        const int jt = (SPW * wave + i) % NJT;
+        const int ct = (wave / NJT) * SPW + i;
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(sEGam + 16 * ct + 4 * lg);
         f32x4 s = Sacc[i] * gam;
 #pragma unroll
         for (int q = 0; q < NKT; ++q) {
-          s = M::mma(ak[q], M::ld(sUT + (16 * jt + l16) * LDU + q * KS + kofs), s);
-          if constexpr (BF16) s = M::mma(ak[q], M::ld(sUT2 + (16 * jt + l16) * LDU + q * KS + kofs), s);
+          const frag ak = M::ld(sKbT + (16 * ct + l16) * LDC + q * KS + kofs);
+          s = M::mma(ak, uh[q], s);
+          if constexpr (BF16) s = M::mma(ak, ul[q], s);
         }
         Sacc[i] = s;
       }
@@ -814,7 +829,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
       float* dst = p.ck + ((b * nck + ck_idx) * H + h) * (int64_t)DK * DV;
 #pragma unroll
       for (int i = 0; i < SPW; ++i) {
-        const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
+        const int ct = (wave / NJT) * SPW + i, jt = wave % NJT;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
           dst[(int64_t)(16 * ct + 4 * lg + m) * DV + j0 + 16 * jt + l16] = Sacc[i][m];
@@ -838,7 +853,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   if (dst) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-      const int tt = SPW * wave + i, ct = tt / NJT, jt = tt % NJT;
+      const int ct = (wave / NJT) * SPW + i, jt = wave % NJT;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         dst[(int64_t)(16 * ct + 4 * lg + m) * ld + j0 + 16 * jt + l16] = Sacc[i][m];
