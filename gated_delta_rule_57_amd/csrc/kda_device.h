@@ -20,7 +20,8 @@ constexpr float kLogDecayFloor = -5.0f;
 
 // min(max(g, -5), 0) that keeps NaN (fmaxf/fminf would drop it).
 __device__ __forceinline__ float clamp_log_decay(float g) {
-  return (g != g) ? g : fminf(fmaxf(g, kLogDecayFloor), 0.0f);
+  // median of three: one instruction, no NaN canonicalisation; NaN passed through
+  return (g != g) ? g : __builtin_amdgcn_fmed3f(g, kLogDecayFloor, 0.0f);
 }
 
 // Log-decay in base-2 units from a raw decay logit a: clamp(-softplus(a)) * log2(e),
@@ -31,7 +32,7 @@ __device__ __forceinline__ float clamp_log_decay(float g) {
 // become 0 (a relative decay error below 1e-7).
 __device__ __forceinline__ float gamma_from_logit(float a) {
   const float t = -__builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(a * kLog2e));
-  return (a != a) ? a : fminf(fmaxf(t, kLogDecayFloor * kLog2e), 0.0f);
+  return (a != a) ? a : __builtin_amdgcn_fmed3f(t, kLogDecayFloor * kLog2e, 0.0f);
 }
 
 // 2^x on the hardware transcendental unit.
