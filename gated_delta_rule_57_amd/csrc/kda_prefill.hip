@@ -665,6 +665,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     // tile, all in float32 MFMA from registers (no triangular factor is formed).
     // Each wave reads its whole column tile of Z before writing U over it.
     if (wave < NJT) {
+      __builtin_amdgcn_s_setprio(2);  // the substitution chains are this phase's critical path
       const int jt = wave, jv = 16 * jt + l16;
       // the left operands, in the transposed result layout: lane holds X[l16][4 lg + kb]
       auto left = [&](const float* X, int ldx, int rx, int cx) {
@@ -705,6 +706,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
           if constexpr (BF16) sUT2[jv * LDU + i0 + m] = from_f32<op_t>(u[m] - to_f32(uh));
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     } else if (BF16 && wave >= 4) {
       // meanwhile: P (float32) -> hi / lo bfloat16 operand rows in place (hi at element
       // 0 of the row, lo at element kC); a wave owns whole rows, four lanes per row, so
