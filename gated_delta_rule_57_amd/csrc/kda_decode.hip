@@ -127,12 +127,18 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
 // single-token kernel does) across the tokens.  The inputs of up to KB tokens are
 // loaded into shared memory at once (with the decays and k.q computed there), so
 // the token loop has no global loads and two barriers per token.
+// 512 threads (eight waves) keep RPT = 16 or fewer state values x 4 columns per
+// thread: eight waves per SIMD fit for a commit, five for a verification.
+// 256-thread workgroups (twice the values per thread, fewer waves) measured 5-7%
+// slower; 1024 no faster for a commit and far slower for a verification.
+constexpr int kMultiThreads = 512;
+
 template <typename TIn, typename TOut, int DK, int DV, bool COMMIT>
-__global__ void __launch_bounds__(256) multi_token_kernel(
+__global__ void __launch_bounds__(kMultiThreads) multi_token_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ beta, const int32_t* __restrict__ accept,
     float* __restrict__ state, TOut* __restrict__ o, int64_t N, int64_t K, int64_t H) {
-  constexpr int NT = 256, KB = 8;
+  constexpr int NT = kMultiThreads, KB = 8;
   constexpr int CG = DV / 4, RG = NT / CG, RPT = DK / RG;
   static_assert(RPT * RG == DK && CG * RG == NT, "thread layout");
   constexpr bool WANT_O = !COMMIT;
@@ -275,7 +281,7 @@ template <typename TIn, typename TOut, bool COMMIT>
 hipError_t launch_multi(const void* q, const void* k, const void* v, const void* g,
                         const void* beta, const int32_t* accept, float* state, void* o, int64_t N,
                         int64_t K, int64_t H, int dk, int dv, hipStream_t s) {
-  const dim3 grid((unsigned)(N * H)), block(256);
+  const dim3 grid((unsigned)(N * H)), block(kMultiThreads);
 #define KDA_MULTI(DK_, DV_)                                                                     \
   multi_token_kernel<TIn, TOut, DK_, DV_, COMMIT><<<grid, block, 0, s>>>(                       \
       (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, accept, state, \
