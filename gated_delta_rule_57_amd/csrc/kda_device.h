@@ -37,7 +37,6 @@ __device__ __forceinline__ float gamma_from_logit(float a) {
 
 // 2^x on the hardware transcendental unit.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ f32x2 exp2_hw2(f32x2 x) { return f32x2{exp2_hw(x.x), exp2_hw(x.y)}; }
 
 // Two adjacent elements in one register: a bfloat16 pair (low half = lower
 // address) or a float32 pair.  pack2 rounds to nearest even.
