@@ -125,10 +125,10 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
 //
 // One workgroup per (sequence, head) keeps the state slice in registers (as the
 // single-token kernel does) across the tokens.  The inputs of up to KB tokens are
-// loaded into shared memory at once (with the decays and k.q computed there), so
-// the token loop has no global loads and two barriers per token.
-// 512 threads (eight waves) keep RPT = 16 or fewer state values x 4 columns per
-// thread: eight waves per SIMD fit for a commit, five for a verification.
+// loaded into shared memory at once (with the cumulative decays and k.q computed
+// there), so the token loop has no global loads and two barriers per token.
+// 512 threads (eight waves) keep RPT = 8 or fewer state rows x 4 columns per
+// thread: eight waves per SIMD fit for a commit, six for a verification (below).
 // 256-thread workgroups (twice the values per thread, fewer waves) measured 5-7%
 // slower; 1024 no faster for a commit and far slower for a verification.
 constexpr int kMultiThreads = 512;
@@ -156,8 +156,13 @@ multi_token_kernel(
     if (steps == 0) return;
   }
   const int t = threadIdx.x, cg = t % CG, rg = t / CG;
-  __shared__ float s_q[WANT_O ? KB : 1][DK], s_k[KB][DK], s_dec[KB][DK], s_v[KB][DV];
-  __shared__ float s_beta[KB], s_kq[KB];
+  // Inside a block the state is carried undecayed, S~ = Diag(Gamma_j)^-1 S with Gamma_j
+  // the block's cumulative decay through token j: the decay moves from every state
+  // element onto the token's key and query vectors (k Gamma_j, q Gamma_j, k / Gamma_j),
+  // and the state is decayed once at the end of the block.  Gamma_j >= 2^(-5 log2e KB),
+  // so 1 / Gamma_j stays a normal float.
+  __shared__ float s_qg[WANT_O ? KB : 1][DK], s_kg[KB][DK], s_ki[KB][DK], s_v[KB][DV];
+  __shared__ float s_ge[DK], s_beta[KB], s_kq[KB];
   __shared__ float s_part_a[RG][DV], s_part_b[WANT_O ? RG : 1][DV];
   __shared__ float s_u[DV];
 
@@ -169,13 +174,14 @@ multi_token_kernel(
   for (int64_t j0 = 0; j0 < steps; j0 += KB) {
     const int nb = (int)((steps - j0) < KB ? (steps - j0) : KB);
     if (j0 > 0) __syncthreads();  // the previous block is done with the inputs
-    // this block's inputs: token j of the draft is [n, j, h]
+    // this block's inputs (token j of the draft is [n, j, h]), raw: k, g (in the slot of
+    // k / Gamma), q, v, beta
     for (int e = t; e < nb * DK; e += NT) {
       const int j = e / DK, c = e % DK;
       const int64_t off = ((n * K + j0 + j) * H + h) * DK + c;
-      if (WANT_O) s_q[j][c] = to_f32(q[off]);
-      s_k[j][c] = to_f32(k[off]);
-      s_dec[j][c] = exp2_hw(clamp_log_decay(to_f32(g[off])) * kLog2e);
+      if (WANT_O) s_qg[j][c] = to_f32(q[off]);
+      s_kg[j][c] = to_f32(k[off]);
+      s_ki[j][c] = to_f32(g[off]);
     }
     for (int e = t; e < nb * DV; e += NT) {
       const int j = e / DV, c = e % DV;
@@ -183,12 +189,25 @@ multi_token_kernel(
     }
     if (t < nb) s_beta[t] = to_f32(beta[(n * K + j0 + t) * H + h]);
     __syncthreads();
-    if (WANT_O) {  // k . q of each token: wave w takes tokens w, w + 4
+    if (t < DK) {  // one thread per key channel: the cumulative decay over the block
+      const int c = t;
+      float G = 1.f;
+      for (int j = 0; j < nb; ++j) {
+        G *= exp2_hw(clamp_log_decay(s_ki[j][c]) * kLog2e);
+        const float kk = s_kg[j][c];
+        s_kg[j][c] = kk * G;
+        s_ki[j][c] = kk * __builtin_amdgcn_rcpf(G);
+        if (WANT_O) s_qg[j][c] *= G;
+      }
+      s_ge[c] = G;
+    }
+    __syncthreads();
+    if (WANT_O) {  // k . q of each token (= (q Gamma) . (k / Gamma)): one wave per token
       const int w = t >> 6, l = t & 63;
       for (int j = w; j < nb; j += NT / 64) {
         float x = 0.f;
 #pragma unroll
-        for (int c = l; c < DK; c += 64) x += s_q[j][c] * s_k[j][c];
+        for (int c = l; c < DK; c += 64) x += s_qg[j][c] * s_ki[j][c];
         x = wave_sum(x);
         if (l == 0) s_kq[j] = x;
       }
@@ -199,17 +218,13 @@ multi_token_kernel(
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int c = rg + RG * i;
-        const float d = s_dec[j][c], kc = s_k[j][c];
-        S[i].x *= d;
-        S[i].y *= d;
-        S[i].z *= d;
-        S[i].w *= d;
+        const float kc = s_kg[j][c];
         pa.x += kc * S[i].x;
         pa.y += kc * S[i].y;
         pa.z += kc * S[i].z;
         pa.w += kc * S[i].w;
         if (WANT_O) {
-          const float qc = s_q[j][c];
+          const float qc = s_qg[j][c];
           pb.x += qc * S[i].x;
           pb.y += qc * S[i].y;
           pb.z += qc * S[i].z;
@@ -234,7 +249,7 @@ multi_token_kernel(
       const float4 u4 = *reinterpret_cast<const float4*>(&s_u[4 * cg]);
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const float kc = s_k[j][rg + RG * i];
+        const float kc = s_ki[j][rg + RG * i];
         S[i].x += kc * u4.x;
         S[i].y += kc * u4.y;
         S[i].z += kc * u4.z;
@@ -243,6 +258,16 @@ multi_token_kernel(
       // the next token's partial sums overwrite s_part_* only after everyone has
       // read them (they were read before the barrier above); s_u is rewritten after
       // the next token's first barrier, by which time this update is done
+    }
+    if (COMMIT || j0 + KB < steps) {  // back to the decayed state: S = Diag(Gamma_last) S~
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float ge = s_ge[rg + RG * i];
+        S[i].x *= ge;
+        S[i].y *= ge;
+        S[i].z *= ge;
+        S[i].w *= ge;
+      }
     }
   }
   if (COMMIT) {

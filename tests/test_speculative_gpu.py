@@ -92,7 +92,8 @@ def test_full_accept_equals_single_steps(dtype):
     e_o = oracle.rel_l2(_np(o), _np(o_steps))
     e_s = oracle.rel_l2(_np(state), _np(ref))
     print(f"[spec] {dtype}: verify vs steps o {e_o:.3e}, commit vs steps state {e_s:.3e}", flush=True)
-    # the same per-token arithmetic; only the compiler's scheduling of two copies differs
+    # the same recurrence; the draft kernel carries the state undecayed inside a block of
+    # tokens (decays on the key and query vectors), so only float32 rounding differs
     assert e_o <= 1e-6 and e_s <= 1e-6
 
 
