@@ -119,3 +119,31 @@ def test_rejected_draft_then_new_draft():
     e = oracle.rel_l2(_np(o2), o_r)
     print(f"[spec] reject then redraft: o {e:.3e}", flush=True)
     assert e <= 3e-3
+
+
+def test_full_size_draft_workload_sampled_sequences():
+    """The launch the bench times: 256 sequences x 32 heads, K = 4 drafts, d = 128,
+    bfloat16 in and out, inputs drawn on the device with the workload's laws (the state
+    scaled to the size a long prefill leaves).  Every sequence runs; 16 of them, whose
+    accept counts cover 0..K and one past K, are checked against the oracle run on their
+    inputs, outputs and committed states."""
+    N, K, H = 256, 4, 32
+    w = synth.PREFILL_B4_T4096.replace(B=N, T=K, H=H)
+    d = synth.device_prefill_inputs(w, DEV)
+    state = 25.0 * d["s0"]
+    seqs = np.arange(0, N, 17)[:16]
+    x = {n: _np(d[n][seqs]) for n in ("q", "k", "v", "g", "beta")}
+    s0 = _np(state[seqs])
+    accept = (np.arange(N) % (K + 2)).astype(np.int32)
+    assert set(accept[seqs]) == set(range(K + 2))
+    o = kda.kda_recurrent_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], state)
+    kda.kda_recurrent_commit(d["k"], d["v"], d["g"], d["beta"], torch.from_numpy(accept).to(DEV),
+                             state)
+    torch.cuda.synchronize()
+    o_r, s_r = _oracle_steps(x, s0, np.minimum(accept[seqs], K))
+    e_o = oracle.rel_l2(_np(o[seqs]), o_r)
+    e_s = oracle.rel_l2(_np(state[seqs]), s_r)
+    print(f"[spec] N{N} H{H} K{K} bf16, 16 sampled sequences: o {e_o:.3e} state {e_s:.3e}",
+          flush=True)
+    assert o.dtype == torch.bfloat16 and bool(torch.isfinite(o.float()).all())
+    assert e_o <= 3e-3 and e_s <= 3e-3
