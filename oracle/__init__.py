@@ -39,5 +39,6 @@ from .kda import (  # noqa: F401
     kda_decode_step,
     kda_forward,
     kda_forward_heads_parallel,
+    one_hot_key_rows,
     rel_l2,
 )

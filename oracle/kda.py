@@ -132,3 +132,32 @@ def rel_l2(x, ref) -> float:
     den = np.linalg.norm(ref.ravel())
     num = np.linalg.norm((x - ref).ravel())
     return float(num / den) if den > 0 else float(num)
+
+
+def one_hot_key_rows(rows0, g, hit, beta, v):
+    """Rows of the KDA state when every key is a one-hot vector (closed form).
+
+    With k_t = e_{c_t}, S^T k_t is row c_t of the decayed state, so the delta
+    update touches that row alone: every row c is an independent gated moving
+    average,
+
+        S[c] <- exp(g'_{t,c}) S[c]                       (decay, g' clamped as above)
+        S[c] <- (1 - beta_t) S[c] + beta_t v_t           (only when c == c_t)
+
+    and a one-hot query e_r reads o_t = S_t[r].  Follows from the recurrence in
+    the package docstring; pinned against :func:`kda_forward` in the tests.
+
+    rows0 [R, dv] entry rows; g [T, R] their log-decays; hit [T, R] bool (the
+    token's key is that row's channel); beta [T, R]; v [T, R, dv] the value vector
+    of each row's head.  Returns (trajectory [T, R, dv] = rows after each token,
+    final rows [R, dv]), float64.
+    """
+    x = np.array(rows0, dtype=np.float64)
+    keep = np.exp(clamp_log_decay(g))
+    hb = np.where(np.asarray(hit, bool), np.asarray(beta, np.float64), 0.0)
+    v = np.asarray(v, np.float64)
+    traj = np.empty((keep.shape[0],) + x.shape)
+    for t in range(keep.shape[0]):
+        x = ((1.0 - hb[t]) * keep[t])[:, None] * x + hb[t][:, None] * v[t]
+        traj[t] = x
+    return traj, x

@@ -270,3 +270,37 @@ def device_decode_inputs(w: Workload, steps: int, device, seed_offset: int = 0):
     else:
         d["s0"] = torch.zeros((w.B, w.H, w.dk, w.dv), device=device)
     return d
+
+
+def device_one_hot_inputs(w: Workload, device, seed_offset: int = 0, memory_tokens: int = 4096):
+    """A prefill workload's shapes and laws with one-hot keys and queries, on the device.
+
+    Keys: k_t = e_{c_t} with c_t uniform over channels 0 .. dk-3 for every token
+    and head, except that inside the first ``memory_tokens`` tokens every 64th
+    token's key is channel dk-2 instead.  Channels dk-2 and dk-1 get log-decay 0
+    (no decay): dk-2 is written early and then held for the rest of the sequence,
+    dk-1 is never written.  Queries: q_t = e_{r_h}, one read channel r_h per head,
+    uniform over 0 .. dk-3.  v, beta, the other channels' log-decays and the
+    initial state follow the workload's laws.  One-hot vectors are exact in every
+    storage dtype.
+
+    Returns the tensors of :func:`device_prefill_inputs` plus ``chan`` [B,T,H]
+    (int64, the key channel of each token) and ``read`` [H] (int64).
+    """
+    import torch
+
+    d = device_prefill_inputs(w, device, seed_offset)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(3_000_017 * (w.seed + 1) + seed_offset)
+    B, T, H, dk = w.B, w.T, w.H, w.dk
+    dt = torch_dtype(w.dtype)
+    chan = torch.randint(0, dk - 2, (B, T, H), generator=gen, device=device)
+    chan[:, : min(memory_tokens, T) : 64] = dk - 2
+    read = torch.randint(0, dk - 2, (H,), generator=gen, device=device)
+    k = torch.zeros((B, T, H, dk), dtype=dt, device=device)
+    k.scatter_(-1, chan.unsqueeze(-1), 1.0)
+    q = torch.zeros((B, T, H, dk), dtype=dt, device=device)
+    q.scatter_(-1, read.view(1, 1, H, 1).expand(B, T, H, 1), 1.0)
+    d["g"][..., dk - 2:] = 0.0
+    d.update(q=q, k=k, chan=chan, read=read)
+    return d

@@ -181,6 +181,44 @@ def test_closed_form_one_hot_keys_are_gated_emas():
     np.testing.assert_allclose(S, np.array(rows), rtol=0, atol=1e-12)
 
 
+def test_one_hot_row_closed_form_follows_the_hand_loop():
+    """oracle.one_hot_key_rows (the closed form used at the million-token length)
+    against a plain scalar loop of the gated moving averages, written out here, with
+    log-decays below the floor and above zero (both clamped) and rows never hit."""
+    rng = np.random.default_rng(16)
+    T, dk, dv = 60, 6, 3
+    chan = rng.integers(0, dk - 1, T)            # the last channel is never hit
+    g = rng.uniform(-7.0, 0.5, (T, dk))
+    g[:, 2] = 0.0                                # a channel that never decays
+    beta = rng.uniform(0.0, 1.0, T)
+    v = rng.standard_normal((T, dv))
+    s0 = rng.standard_normal((dk, dv))
+    rows = [list(s0[c]) for c in range(dk)]
+    want = np.empty((T, dk, dv))
+    for t in range(T):
+        for c in range(dk):
+            keep = math.exp(min(max(g[t, c], -5.0), 0.0))
+            for j in range(dv):
+                x = keep * rows[c][j]
+                if c == chan[t]:
+                    x = x + beta[t] * (v[t, j] - x)
+                rows[c][j] = x
+                want[t, c, j] = x
+    hit = chan[:, None] == np.arange(dk)[None, :]
+    traj, fin = oracle.one_hot_key_rows(s0, g, hit, np.repeat(beta[:, None], dk, 1),
+                                        np.repeat(v[:, None], dk, 1))
+    np.testing.assert_allclose(traj, want, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(fin, want[-1], rtol=1e-13, atol=1e-15)
+    # the row that is never hit only decays
+    np.testing.assert_allclose(fin[dk - 1], s0[dk - 1] * np.prod(np.exp(np.clip(g[:, dk - 1],
+                                                                             -5.0, 0.0))),
+                               rtol=1e-12)
+    # the undecayed channel: its row is a plain beta-weighted average, unchanged between hits
+    last = np.nonzero(chan == 2)[0]
+    if len(last):
+        assert np.array_equal(fin[2], traj[last[-1], 2])
+
+
 def test_clamp_is_idempotent_and_nan_propagates():
     rng = np.random.default_rng(15)
     q, k, v, g, beta, s0 = _rand_head(rng, 5, 4, 4)

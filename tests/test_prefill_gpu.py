@@ -114,3 +114,49 @@ def test_million_token_prefix_checkpoint():
     assert bool(torch.isfinite(sf).all()) and bool(torch.isfinite(o.float()).all())
     # the last checkpoint is the final state
     assert torch.equal(ck[:, -1], sf)
+
+
+def test_million_token_one_hot_keys_full_length():
+    """1,048,576 tokens x 16 heads with one-hot keys and queries (the rest as the
+    million-token workload): every state row is then an independent gated moving
+    average (oracle.one_hot_key_rows), so outputs and final states can be checked
+    over the whole length, across every segment the library cuts.  Tracked per
+    head: the read row (all outputs), a row written in the first 4096 tokens and
+    never decayed (carried across all segments), and a row never written and never
+    decayed (must come out as the initial state, bit for bit)."""
+    w = synth.MILLION_TOKEN
+    print(f"[prefill] one-hot keys B{w.B} T{w.T} H{w.H} d{w.dk}", flush=True)
+    d = synth.device_one_hot_inputs(w, DEV)
+    o, sf, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(sf).all()) and bool(torch.isfinite(o.float()).all())
+    dk = w.dk
+    heads = [0, 5, 10, 15]
+    read = d["read"].cpu().tolist()
+    rows = [(h, c) for h in heads for c in (read[h], dk - 2, dk - 1)]
+    hh = torch.tensor([h for h, _ in rows], device=DEV)
+    cc = torch.tensor([c for _, c in rows], device=DEV)
+    g_rows = d["g"][0][:, hh, cc].double().cpu().numpy()
+    hit = (d["chan"][0][:, hh] == cc).cpu().numpy()
+    beta = d["beta"][0][:, hh].double().cpu().numpy()
+    rows0 = d["s0"][0, hh, cc].double().cpu().numpy()
+    v_h = d["v"][0][:, heads].float().cpu().numpy()             # [T, 4, dv]
+    o_h = o[0][:, heads].float().cpu().numpy()                  # [T, 4, dv]
+    head_of_row = [heads.index(h) for h, _ in rows]
+    read_rows = [3 * i for i in range(len(heads))]               # trajectory rows read by q
+    x, num, den = rows0, 0.0, 0.0
+    for t0 in range(0, w.T, synth.BLOCK_T):
+        t1 = min(w.T, t0 + synth.BLOCK_T)
+        traj, x = oracle.one_hot_key_rows(x, g_rows[t0:t1], hit[t0:t1], beta[t0:t1],
+                                          v_h[t0:t1][:, head_of_row])
+        ref = traj[:, read_rows]
+        num += float(np.sum((o_h[t0:t1] - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+    e_o = (num / den) ** 0.5
+    got = sf[0, hh, cc].double().cpu().numpy()
+    e_s = oracle.rel_l2(got, x)
+    print(f"[prefill]   one-hot full length: o (tracked heads) {e_o:.3e} "
+          f"state rows {e_s:.3e}", flush=True)
+    assert e_o <= 3e-3 and e_s <= 3e-3
+    # the never-written, never-decayed row of every head is the initial state exactly
+    assert torch.equal(sf[0, :, dk - 1], d["s0"][0, :, dk - 1])
