@@ -83,8 +83,11 @@ int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, boo
     const int64_t segc = (nch + want - 1) / want;  // chunks per segment
     const int64_t n = (nch + segc - 1) / segc;     // segments that length gives
     if (n != want) continue;
+    // summaries: zero-start states of segments 0 .. n-2 (segment 0 from the initial
+    // state, writing its outputs too) and transitions of segments 1 .. n-2; outputs:
+    // segments 1 .. n-1
     const double summary = rounds(B * H * ((n - 1) * (ns + np) - np)) * (double)segc;
-    const double outputs = rounds(B * n * H * ns) * (double)segc;
+    const double outputs = rounds(B * (n - 1) * H * ns) * (double)segc;
     // a scan step costs about a third of a chunk step; the two extra launches
     // about a chunk step each
     const double extra = 0.3 * (double)n + 2.0;
@@ -198,7 +201,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
     s1.seg_p = seg_p;
     hipError_t e = kda::chunk_fwd(s1, dk, dv, bf16, out == KDA_BF16, st);
     if (e == hipSuccess)
-      e = kda::segment_scan(initial_state, seg_z, seg_p, seg_in, B, H, nseg, dk, dv, st);
+      e = kda::segment_scan(seg_z, seg_p, seg_in, B, H, nseg, dk, dv, st);
     if (e != hipSuccess) return KDA_ERR_HIP;
     a.seg_in = seg_in;
   }

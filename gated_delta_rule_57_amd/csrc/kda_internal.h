@@ -52,10 +52,10 @@ int64_t prefill_grid(int64_t units, int slices);
 hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool out_bf16,
                      hipStream_t s);
 
-// Entry states of the segments: seg_in[b, 0, h] = s0 (zeros if NULL),
-// seg_in[b, 1, h] = seg_z[b, 0, h], seg_in[b, j+1, h] = seg_p[b, j, h] seg_in[b, j, h]
-// + seg_z[b, j, h].  float32 throughout.
-hipError_t segment_scan(const float* s0, const float* seg_z, const float* seg_p, float* seg_in,
+// Entry states of the segments after the first: seg_in[b, 1, h] = seg_z[b, 0, h] (the
+// summary of segment 0 starts from the initial state), seg_in[b, j+1, h] =
+// seg_p[b, j, h] seg_in[b, j, h] + seg_z[b, j, h].  Slot 0 is not written.  float32.
+hipError_t segment_scan(const float* seg_z, const float* seg_p, float* seg_in,
                         int64_t B, int64_t H, int64_t nseg, int dk, int dv, hipStream_t s);
 
 // K draft tokens per sequence ([N, K, H, .] inputs): commit = false writes o for

@@ -218,25 +218,31 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 
   // Workgroup -> (unit, slice), unit = (b, segment, h): consecutive workgroups
   // are dealt round-robin to the 8 XCDs, so give all slices of a unit the same
-  // XCD (and L2).  The summary pass (mode 1) adds DK / DVS slices that carry
-  // the segment's transition matrix, and covers every segment but the last.
+  // XCD (and L2).  With several segments each launch covers all but one: the
+  // summary pass (mode 1) every segment but the last, with DK / DVS more slices
+  // that carry the segment's transition matrix; the output pass (mode 0) every
+  // segment but the first, whose outputs the summary pass already wrote (its
+  // workgroups start from the true initial state).
   constexpr int NPSL = DK / DVS;
   const int nsl = p.mode ? NSLICE + NPSL : NSLICE;
-  const int64_t nsg = p.mode ? p.nseg - 1 : p.nseg;
+  const int64_t nsg = p.nseg > 1 ? p.nseg - 1 : 1;
+  const int64_t seg0 = (p.mode == 0 && p.nseg > 1) ? 1 : 0;  // first segment covered
   const int64_t x = blockIdx.x;
   const int64_t grp = x / (8 * nsl);
   const int gi = (int)(x % (8 * nsl));
   const int64_t unit = grp * 8 + (gi % 8);
   const int slice = gi / 8;
   if (unit >= p.B * nsg * p.H) return;
-  const int64_t h = unit % p.H, bj = unit / p.H, seg = bj % nsg, b = bj / nsg;
+  const int64_t h = unit % p.H, bj = unit / p.H, seg = bj % nsg + seg0, b = bj / nsg;
   const bool pmode = slice >= NSLICE;  // transition workgroup (mode 1 only)
   if (pmode && seg == 0) return;       // segment 0's transition is never used
   const int j0 = (pmode ? slice - NSLICE : slice) * DVS;
   const int64_t T = p.T, H = p.H;
   const int64_t tb = seg * p.seg_len;                             // first token
   const int64_t te = (T - tb) < p.seg_len ? T : tb + p.seg_len;   // one past the last
-  const bool emit = p.mode == 0;
+  // outputs (o, checkpoints, the final state) come from the output pass and, for
+  // segment 0, from the summary pass's workgroups that walk it from the initial state
+  const bool emit = p.mode == 0 || (seg == 0 && !pmode);
 
   const TIn* gq = reinterpret_cast<const TIn*>(p.q);
   const TIn* gk = reinterpret_cast<const TIn*>(p.k);
@@ -250,10 +256,11 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // ---- state slice in accumulators: a wave holds one value-column tile jt = wave % NJT
   // and SPW key-channel tiles ct = (wave / NJT) SPW + i
   const float* src = nullptr;  // entry state (row stride DV), NULL = zeros
-  if (emit)
-    src = p.nseg > 1 ? p.seg_in + seg_unit * DK * DV : (p.s0 ? p.s0 + head_off : nullptr);
-  else if (seg == 0 && p.s0)
+  if (seg > 0) {  // output pass: the scanned entry state; summary pass: zeros (or identity)
+    if (p.mode == 0) src = p.seg_in + seg_unit * DK * DV;
+  } else if (p.s0) {
     src = p.s0 + head_off;
+  }
   f32x4 Sacc[SPW];
 #pragma unroll
   for (int i = 0; i < SPW; ++i) {
@@ -844,7 +851,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // the segment summary (mode 1; transitions have row stride DK)
   float* dst = nullptr;
   int64_t ld = DV;
-  if (emit) {
+  if (p.mode == 0) {
     if (seg == p.nseg - 1 && p.s_final) dst = p.s_final + head_off;
   } else if (pmode) {
     dst = p.seg_p + seg_unit * DK * DK;
@@ -871,7 +878,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                                      Lay::TOTAL);
   if (e != hipSuccess) return e;
   constexpr int NSLICE = DV / DVS, NPSL = DK / DVS;
-  const int64_t units = a.B * (a.mode ? a.nseg - 1 : a.nseg) * a.H;
+  const int64_t units = a.B * (a.nseg > 1 ? a.nseg - 1 : 1) * a.H;
   const int64_t grid = prefill_grid(units, a.mode ? NSLICE + NPSL : NSLICE);
   kern<<<dim3((unsigned)grid), dim3(512), Lay::TOTAL, stream>>>(a);
   return hipGetLastError();

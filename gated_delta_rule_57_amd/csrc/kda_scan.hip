@@ -19,7 +19,7 @@
 namespace kda {
 
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) segment_scan_kernel(const float* s0, const float* seg_z,
+__global__ void __launch_bounds__(256) segment_scan_kernel(const float* seg_z,
                                                            const float* seg_p, float* seg_in,
                                                            int64_t H, int64_t nseg) {
   constexpr int NC = 32;                   // state columns per workgroup
@@ -37,18 +37,13 @@ __global__ void __launch_bounds__(256) segment_scan_kernel(const float* s0, cons
     return base + ((b * nseg + j) * H + h) * (int64_t)DK * DV + cb;
   };
 
-  // slot 0: the sequence's initial state; slot 1: the state after segment 0
-  const float* first = s0 ? s0 + (b * H + h) * (int64_t)DK * DV + cb : nullptr;
+  // slot 1: the state after segment 0 (its summary walked it from the initial
+  // state); slot 0 stays unused, segment 0 being walked by the summary pass itself
   for (int e = tid; e < DK * NC / 4; e += 256) {
     const int r = e / (NC / 4), c = 4 * (e % (NC / 4));
-    const float4 x = first ? *reinterpret_cast<const float4*>(first + (int64_t)r * DV + c)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(blk(seg_in, 0) + (int64_t)r * DV + c) = x;
-    if (nseg > 1) {
-      const float4 z = *reinterpret_cast<const float4*>(blk(seg_z, 0) + (int64_t)r * DV + c);
-      *reinterpret_cast<float4*>(blk(seg_in, 1) + (int64_t)r * DV + c) = z;
-      *reinterpret_cast<float4*>(&sS[r][c]) = z;
-    }
+    const float4 z = *reinterpret_cast<const float4*>(blk(seg_z, 0) + (int64_t)r * DV + c);
+    *reinterpret_cast<float4*>(blk(seg_in, 1) + (int64_t)r * DV + c) = z;
+    *reinterpret_cast<float4*>(&sS[r][c]) = z;
   }
 
   for (int64_t j = 1; j + 1 < nseg; ++j) {
@@ -89,20 +84,20 @@ __global__ void __launch_bounds__(256) segment_scan_kernel(const float* s0, cons
 }
 
 template <int DK, int DV>
-static hipError_t launch_scan(const float* s0, const float* seg_z, const float* seg_p,
+static hipError_t launch_scan(const float* seg_z, const float* seg_p,
                               float* seg_in, int64_t B, int64_t H, int64_t nseg, hipStream_t s) {
   const int64_t grid = B * H * (DV / 32);
-  segment_scan_kernel<DK, DV><<<dim3((unsigned)grid), dim3(256), 0, s>>>(s0, seg_z, seg_p, seg_in,
+  segment_scan_kernel<DK, DV><<<dim3((unsigned)grid), dim3(256), 0, s>>>(seg_z, seg_p, seg_in,
                                                                          H, nseg);
   return hipGetLastError();
 }
 
-hipError_t segment_scan(const float* s0, const float* seg_z, const float* seg_p, float* seg_in,
+hipError_t segment_scan(const float* seg_z, const float* seg_p, float* seg_in,
                         int64_t B, int64_t H, int64_t nseg, int dk, int dv, hipStream_t s) {
-  if (dk == 128 && dv == 128) return launch_scan<128, 128>(s0, seg_z, seg_p, seg_in, B, H, nseg, s);
-  if (dk == 128 && dv == 64) return launch_scan<128, 64>(s0, seg_z, seg_p, seg_in, B, H, nseg, s);
-  if (dk == 64 && dv == 128) return launch_scan<64, 128>(s0, seg_z, seg_p, seg_in, B, H, nseg, s);
-  return launch_scan<64, 64>(s0, seg_z, seg_p, seg_in, B, H, nseg, s);
+  if (dk == 128 && dv == 128) return launch_scan<128, 128>(seg_z, seg_p, seg_in, B, H, nseg, s);
+  if (dk == 128 && dv == 64) return launch_scan<128, 64>(seg_z, seg_p, seg_in, B, H, nseg, s);
+  if (dk == 64 && dv == 128) return launch_scan<64, 128>(seg_z, seg_p, seg_in, B, H, nseg, s);
+  return launch_scan<64, 64>(seg_z, seg_p, seg_in, B, H, nseg, s);
 }
 
 }  // namespace kda

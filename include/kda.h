@@ -121,13 +121,14 @@ kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const vo
  * same computation as kda_chunk_fwd's single pass.  With several segments
  * three launches are enqueued:
  *   1. every segment but the last is summarised in parallel: Z, the state it
- *      reaches from a zero state (the first segment starts from initial_state),
- *      and P (dk x dk), the product of its tokens' transitions, obtained by
- *      running it from the identity with v = 0;
+ *      reaches from a zero state, and P (dk x dk), the product of its tokens'
+ *      transitions, obtained by running it from the identity with v = 0; the
+ *      first segment instead runs from initial_state and also writes its o and
+ *      checkpoints (it is then done);
  *   2. a prefix scan over segments, S_in(j+1) = P_j S_in(j) + Z_j, gives every
- *      segment's entry state;
- *   3. every segment is run from its entry state, writing o, checkpoints and
- *      (last segment) final_state.
+ *      later segment's entry state;
+ *   3. every segment after the first is run from its entry state, writing o,
+ *      checkpoints and (last segment) final_state.
  * The segment law is the one the orkas.ai blog "Kimi K3 architecture" states
  * for splitting a sequence across devices (section "The cost is paid in the
  * serving stack"); here it spreads few long sequences over the GPU's compute

@@ -41,13 +41,21 @@ def _np(t):
     return t.double().cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("bf16", 128, 128), ("bf16", 64, 128),
-                                         ("bf16", 128, 64), ("f32", 128, 128)])
-def test_verify_and_commit_match_oracle(dtype, dk, dv):
-    N, K, H = 6, 5, 3
+@pytest.mark.parametrize("dtype,dk,dv,K,accept", [
+    ("f32", 64, 64, 5, [0, 1, 2, 3, 5, 9]),  # 9 > K: clamped to K
+    ("bf16", 128, 128, 5, [0, 1, 2, 3, 5, 9]),
+    ("bf16", 64, 128, 5, [0, 1, 2, 3, 5, 9]),
+    ("bf16", 128, 64, 5, [0, 1, 2, 3, 5, 9]),
+    ("f32", 128, 128, 5, [0, 1, 2, 3, 5, 9]),
+    # drafts of more than one 8-token block: accept counts at and around block ends
+    ("bf16", 128, 128, 19, [0, 8, 9, 16, 17, 25]),
+    ("f32", 64, 64, 19, [7, 8, 19, 1, 0, 16]),
+])
+def test_verify_and_commit_match_oracle(dtype, dk, dv, K, accept):
+    N, H = 6, 3
     w = synth.PREFILL_B4_T4096.replace(B=N, H=H, dk=dk, dv=dv, dtype=dtype)
     x, s0 = _draft(w, K, seed=11)
-    accept = np.array([0, 1, 2, 3, 5, 9], dtype=np.int32)  # 9 > K: clamped to K
+    accept = np.array(accept, dtype=np.int32)
     steps = np.minimum(accept, K)
     o_r, s_r = _oracle_steps(x, s0, steps)
     d = synth.to_torch(x, dtype, DEV)
@@ -65,7 +73,8 @@ def test_verify_and_commit_match_oracle(dtype, dk, dv):
     print(f"[spec] {dtype} dk{dk} dv{dv} N{N} K{K}: o {e_o:.3e} state {e_s:.3e}", flush=True)
     assert e_o <= TOL[dtype] and e_s <= TOL[dtype]
     # accept = 0: that sequence's state is bitwise untouched
-    assert torch.equal(state[0], state0[0])
+    for n in np.nonzero(accept == 0)[0]:
+        assert torch.equal(state[n], state0[n])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
