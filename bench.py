@@ -3,7 +3,9 @@
 A step is one kda_chunk_fwd (chunked prefill) over the 4 x 4096-token, 32-head,
 d = 128 bfloat16 workload with a float32 initial state, inputs resident in HBM.
 The same run also times kda_recurrent_step on the 256-sequence decode workload
-(1000 chained steps) and the float64 CPU oracle on a bounded sample.
+(1000 chained steps), speculative verify / commit, the two few-head long-sequence
+prefill workloads (65,536 tokens x 32 heads, 1,048,576 tokens x 16 heads), and the
+float64 CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -176,6 +178,45 @@ def time_speculative(kda, torch, w, K, reps):
     return out
 
 
+def time_long_prefill(kda, torch, w, reps: int = 3):
+    """kda_chunk_fwd on a few-head long-sequence workload with the library's own segment choice:
+    one warm call, then `reps` calls timed together with HIP events on the current stream."""
+    import synth
+
+    d = synth.device_prefill_inputs(w, "cuda")
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device="cuda")
+    sf = torch.empty_like(d["s0"])
+    ws_bytes = kda.kda_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], o=o,
+                          final_state=sf, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    assert bool(torch.isfinite(sf).all()), "non-finite final state"
+    seg = kda.kda_chunk_fwd_segment_tokens(w.B, w.T, w.H, w.dk, w.dv)
+    del d, o, sf, ws
+    torch.cuda.empty_cache()
+    nbytes = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    flops = prefill_flops_per_token_head(w.dk, w.dv) * w.B * w.T * w.H
+    gbs, tflops = nbytes / (ms * 1e-3) / 1e9, flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "ms_per_call": ms, "calls_timed": reps,
+            "tokens_per_s": w.B * w.T / (ms * 1e-3), "segments": -(-w.T // seg),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes},
+            "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_MFMA_PEAK_TFLOPS}}
+
+
 def cpu_baseline(w, sample_batches: int):
     """The float64 oracle on the first `sample_batches` sequences of the workload (all heads)."""
     import oracle
@@ -201,6 +242,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the two few-head long-sequence prefill workloads")
     ap.add_argument("--draft", type=int, default=4, help="draft tokens per speculative verify")
     ap.add_argument("--cpu-sample-batches", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -280,6 +323,9 @@ def main():
                                 "traffic": measured_traffic("commit"),
                                 "kernel": "multi_token_kernel<bf16,bf16,128,128,commit>",
                                 "algorithmic_bytes_per_launch": cb}}
+    if not args.no_long:
+        line["long_prefill"] = [time_long_prefill(kda, torch, wl)
+                                for wl in (synth.DECAY_FLOOR_T65536, synth.MILLION_TOKEN)]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_batches)
     print(json.dumps(line), flush=True)

@@ -27,8 +27,8 @@ def _ref(x, every=0):
     return o, s, ck
 
 
-def _check(w, out_dtype=None, every=0, tol=None):
-    x = synth.prefill_inputs(w)
+def _check(w, out_dtype=None, every=0, tol=None, x=None):
+    x = synth.prefill_inputs(w) if x is None else x
     print(f"[prefill] {w.name} B{w.B} T{w.T} H{w.H} dk{w.dk} dv{w.dv} {w.dtype} "
           f"out={out_dtype}", flush=True)
     o, s, ck = _gpu(w, x, out_dtype, every)
@@ -74,6 +74,20 @@ def test_bf16_long_memory_fp32_out():
 def test_checkpoints_match_oracle():
     w = synth.PREFILL_B4_T4096.replace(B=2, T=640, H=2)
     _check(w, out_dtype=torch.float32, every=128)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decay_floor_on_every_channel(dtype):
+    """Log-decay -5 on every channel of every token (and -7, clamped to it, on a third of
+    them): every 16-token sub-tile's cumulative log-decay reaches -80, so every diagonal
+    tile carries column factors up to e^80 ~ 5.5e34, the largest the floor allows."""
+    w = (synth.TINY_F32 if dtype == "f32" else synth.PREFILL_B4_T4096).replace(
+        B=1, T=320, H=2, init_state=True)
+    x = synth.prefill_inputs(w)
+    g = np.full_like(x["g"], -5.0)
+    g[..., ::3] = -7.0
+    x["g"] = g
+    _check(w, out_dtype=torch.float32, x=x)
 
 
 def test_tiny_t_below_one_chunk():
