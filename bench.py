@@ -230,9 +230,19 @@ def cpu_baseline(w, sample_batches: int):
     _, procs = oracle.kda_forward_heads_parallel(*args, x["s0"], processes=procs)
     dt = time.perf_counter() - t
     tokens = nb * w.T
+    # one process on a smaller sample (two heads of one sequence), scaled to all heads
+    h1 = min(2, w.H)
+    x1 = {n: v[:1, :, :h1] for n, v in x.items() if n != "s0"}
+    t = time.perf_counter()
+    oracle.kda_forward_heads_parallel(*[x1[n] for n in ("q", "k", "v", "g", "beta")],
+                                      x["s0"][:1, :h1], processes=1)
+    dt1 = time.perf_counter() - t
     return {"value": tokens / dt, "unit": "tokens/s", "cores": procs, "kind": "oracle",
             "sample": f"{nb} of the {w.B} sequences x {w.T} tokens x {w.H} heads "
-                      f"({tokens * w.H} token-heads, {dt:.1f} s wall on {procs} processes)"}
+                      f"({tokens * w.H} token-heads, {dt:.1f} s wall on {procs} processes)",
+            "single_core": {"value": w.T * h1 / w.H / dt1, "unit": "tokens/s",
+                            "sample": f"1 sequence x {w.T} tokens x {h1} heads on one process "
+                                      f"({dt1:.2f} s), scaled to {w.H} heads"}}
 
 
 def main():
