@@ -118,7 +118,22 @@ def time_prefill(kda, torch, w, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     assert bool(torch.isfinite(o.float()).all()), "non-finite prefill output"
-    return ms
+    # the same launch with the last-level cache (256 MB MALL) flushed before each one by a
+    # 512 MiB write, each launch timed on its own
+    # (control: the same single-launch timing without the flush)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold, single = [], []
+    for i in range(10):
+        for flush, out in ((True, cold), (False, single)):
+            if flush:
+                scratch.fill_(i)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+    del scratch
+    return ms, sum(cold) / len(cold), sum(single) / len(single)
 
 
 def time_decode(kda, torch, w, steps, warmup):
@@ -275,7 +290,7 @@ def main():
     import synth
 
     w = synth.PREFILL_B4_T4096
-    ms = time_prefill(kda, torch, w, args.steps, args.warmup)
+    ms, ms_cold, ms_single = time_prefill(kda, torch, w, args.steps, args.warmup)
     toks = w.B * w.T
     flops = prefill_flops_per_token_head(w.dk, w.dv) * toks * w.H
     nbytes = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv)
@@ -303,6 +318,10 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops},
+        "cold_cache": {"ms_per_step": ms_cold, "launches": 10,
+                       "ms_per_step_unflushed": ms_single,
+                       "note": "each launch timed alone after a 512 MiB write that flushes the "
+                               "256 MB MALL; unflushed: the same single-launch timing without it"},
     }
     if not args.no_decode:
         wd = synth.DECODE_N256
