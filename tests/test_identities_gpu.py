@@ -1,5 +1,6 @@
 """Identities of the GPU path that need no oracle: state hand-off, aliasing, determinism,
-the clamp, padding, decode-versus-prefill agreement."""
+the clamp, padding, decode-versus-prefill agreement, exact power-of-two scaling in (v, S0)
+and in q, and affinity in the initial state."""
 import numpy as np
 import pytest
 import torch
@@ -117,3 +118,70 @@ def test_decode_steps_equal_prefill(dtype):
     tol = 1e-5 if dtype == "f32" else 3e-3
     assert oracle.rel_l2(od.double().cpu().numpy(), o.double().cpu().numpy()) <= tol
     assert oracle.rel_l2(st.double().cpu().numpy(), sf.double().cpu().numpy()) <= tol
+
+
+def _w(dtype, T=300, H=3):
+    """Long-memory decays (logits ~ N(-7, 1)), so that the initial state still shapes
+    the final state after T tokens and the identities below test the state too."""
+    base = synth.TINY_F32 if dtype == "f32" else synth.PREFILL_B4_T4096
+    return base.replace(B=2, T=T, H=H, init_state=True, a_law="slow")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seg", [None, 128])
+def test_power_of_two_scaling_of_values_and_state(dtype, seg):
+    """o and the state are linear in (v, S0) jointly; a power-of-two factor is exact in
+    every rounding step (operands, hi / lo splits, accumulations, the output dtype), so
+    scaling v and S0 by 2^k scales o and the final state by 2^k bit for bit - on the
+    single pass and on the segment path."""
+    d = _inputs(_w(dtype))
+    kw = {} if seg is None else {"segment_tokens": seg}
+    o, s, _ = _fwd(d, **kw)
+    for k in (3, -2):
+        f = 2.0 ** k
+        o2, s2, _ = kda.kda_chunk_fwd(d["q"], d["k"], (d["v"].float() * f).to(d["v"].dtype),
+                                      d["g"], d["beta"], d["s0"] * f, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.float(), o.float() * f), k
+        assert torch.equal(s2, s * f), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_query_scaling_scales_outputs_and_leaves_the_state(dtype):
+    """The state never depends on q; o is linear in q: q -> 2q gives 2o bit for bit and
+    the same final state bit for bit."""
+    d = _inputs(_w(dtype))
+    o, s, _ = _fwd(d)
+    o2, s2, _ = kda.kda_chunk_fwd((d["q"].float() * 2).to(d["q"].dtype), d["k"], d["v"], d["g"],
+                                  d["beta"], d["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(s2, s)
+    assert torch.equal(o2.float(), o.float() * 2)
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 3e-3)])
+@pytest.mark.parametrize("seg", [None, 128])
+def test_affine_in_the_initial_state(dtype, tol, seg):
+    """The map S0 -> (o, S_T) is affine (the segment law's S_T = P S0 + Z):
+    F(S1) + F(S2) = F(S1 + S2) + F(0), to rounding."""
+    w = _w(dtype)
+    d = _inputs(w)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    # states of the size a long prefill leaves (sigma 0.5)
+    S1 = 25.0 * d["s0"]
+    S2 = 0.5 * torch.randn(S1.shape, generator=g, device=DEV)
+    kw = {"out_dtype": torch.float32}
+    if seg is not None:
+        kw["segment_tokens"] = seg
+    (o1, s1, _), (o2, s2, _), (o12, s12, _), (o0, s0_, _) = (
+        _fwd(d, s0=x, **kw) for x in (S1, S2, S1 + S2, torch.zeros_like(S1)))
+    torch.cuda.synchronize()
+    lhs_o, rhs_o = (o1 + o2).double(), (o12 + o0).double()
+    lhs_s, rhs_s = (s1 + s2).double(), (s12 + s0_).double()
+    # the initial state must matter, or the state check would hold trivially
+    assert float((s1 - s0_).norm()) > 10 * tol * float(s0_.norm())
+    e_o = float((lhs_o - rhs_o).norm() / rhs_o.norm())
+    e_s = float((lhs_s - rhs_s).norm() / rhs_s.norm())
+    print(f"[identities] affine {dtype} seg={seg}: o {e_o:.2e} state {e_s:.2e}", flush=True)
+    assert e_o <= tol and e_s <= tol
