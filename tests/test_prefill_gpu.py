@@ -174,3 +174,25 @@ def test_million_token_one_hot_keys_full_length():
     assert e_o <= 3e-3 and e_s <= 3e-3
     # the never-written, never-decayed row of every head is the initial state exactly
     assert torch.equal(sf[0, :, dk - 1], d["s0"][0, :, dk - 1])
+
+
+def _random_cases(n=10, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 4 == 0 else "bf16"
+        dk, dv = (64, 64) if dtype == "f32" else [(128, 128), (64, 64), (64, 128), (128, 64)][i % 4]
+        cases.append((dtype, int(rng.integers(1, 4)), int(rng.integers(1, 700)),
+                      int(rng.integers(1, 6)), dk, dv, bool(rng.integers(0, 2)),
+                      ["n02", "n51", "mixed", "slow"][int(rng.integers(0, 4))]))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,B,T,H,dk,dv,init,law", _random_cases())
+def test_seeded_irregular_shapes(dtype, B, T, H, dk, dv, init, law):
+    """Seeded irregular sizes (T from 1 to 699, ragged tails, one to five heads, one to
+    three batch rows, every supported head-dimension pair, with and without an initial
+    state, every decay law) against the oracle, float32 outputs."""
+    base = synth.TINY_F32 if dtype == "f32" else synth.PREFILL_B4_T4096
+    w = base.replace(B=B, T=T, H=H, dk=dk, dv=dv, init_state=init, a_law=law, seed=7 + T)
+    _check(w, out_dtype=torch.float32, tol=5e-3 if (law == "slow" and dtype == "bf16") else None)
