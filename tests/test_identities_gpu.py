@@ -1,6 +1,6 @@
 """Identities of the GPU path that need no oracle: state hand-off, aliasing, determinism,
 the clamp, padding, decode-versus-prefill agreement, exact power-of-two scaling in (v, S0)
-and in q, and affinity in the initial state."""
+and in q, affinity in the initial state, and exact retrieval with beta = 1."""
 import numpy as np
 import pytest
 import torch
@@ -185,3 +185,28 @@ def test_affine_in_the_initial_state(dtype, tol, seg):
     e_s = float((lhs_s - rhs_s).norm() / rhs_s.norm())
     print(f"[identities] affine {dtype} seg={seg}: o {e_o:.2e} state {e_s:.2e}", flush=True)
     assert e_o <= tol and e_s <= tol
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-5), ("bf16", 3e-3)])
+@pytest.mark.parametrize("seg", [None, 128])
+def test_exact_retrieval_with_unit_keys_and_full_writes(dtype, tol, seg):
+    """beta = 1 with a unit-norm key overwrites what the key reads: S_t^T k_t = v_t for any
+    decay and any earlier state.  With q = k the output is therefore v itself, token by
+    token (the retrieval invariant of the pin table, through the whole chunked path)."""
+    w = _w(dtype, T=333).replace(a_law="n02")
+    x = synth.prefill_inputs(w)
+    x["q"] = x["k"]  # unit norm (rounded to the storage dtype: the norm is 1 to rounding)
+    x["beta"] = np.ones_like(x["beta"])
+    d = synth.to_torch(x, w.dtype, DEV)
+    kw = {"out_dtype": torch.float32}
+    if seg is not None:
+        kw["segment_tokens"] = seg
+    o, _, _ = _fwd(d, **kw)
+    torch.cuda.synchronize()
+    # The stored keys are unit vectors only to the storage rounding: the retrieval is then
+    # v + (|k|^2 - 1)(v - S'^T k), off by |k|^2 - 1 (about 4e-4 in bfloat16, 1e-7 in
+    # float32), inside the tolerance.
+    v = d["v"].double()
+    e = float((o.double() - v).norm() / v.norm())
+    print(f"[identities] retrieval {dtype} seg={seg}: |o - v| / |v| = {e:.2e}", flush=True)
+    assert e <= tol
