@@ -300,7 +300,9 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   // Rows past the end of the sequence load the last valid token (always in
   // bounds) and are zeroed when staged, so the loads themselves are branch-free.
   // The loads are issued in four parts spread over the chunk's phases, so that
-  // the memory pipeline is not asked for a whole chunk at once.
+  // the memory pipeline is not asked for a whole chunk at once: v at the top of
+  // the chunk, k after the decay products, q before the row-tile products, g and
+  // beta before the substitution (placements swept; these measured fastest).
   auto prefetch = [&](int64_t t0, int part) {
     const int64_t cb = (b * T + t0) * H + h;
     const int last = (int)((te - t0) < kC ? (te - t0) : kC) - 1;
@@ -496,7 +498,6 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
-    prefetch(tn, 2);
     // ---- A and P tiles, every tile pair one dense product.  Waves 0-3 take the six
     // off-diagonal pairs (two, two, one, one); wave 4 + R takes the diagonal pair
     // (R, R) and inverts I + A_RR right away, keeping the inverse in registers (the
@@ -592,7 +593,6 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
-    prefetch(tn, 3);
     // ---- deferred operands into the released region (channel-major threads):
     // k 2^(G_end - G) transposed (token-contiguous: one piece per channel), k 2^G and
     // q 2^G row-major.
@@ -631,6 +631,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
+    prefetch(tn, 2);
     // ---- per row tile, over the key channels: Y = Kc S and Qc S; Z = V - Y, stored
     // transposed and times beta (float32) for the substitution
     constexpr int NKT = kC / KS;  // k-steps over the chunk's tokens
@@ -670,6 +671,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     __syncthreads();
 
+    prefetch(tn, 3);
     // ---- U = (I + A)^-1 Diag(beta) Z by block forward substitution over the four
     // row tiles, U_R = D_R (beta Z_R - sum_{J<R} A_RJ U_J): one wave per value-column
     // tile, all in float32 MFMA from registers (no triangular factor is formed).
