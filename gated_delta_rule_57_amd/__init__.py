@@ -102,6 +102,44 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape, dtype, device) -> None:
+    """Raise ValueError unless tensor t has exactly this shape, dtype and device.  The C
+    ABI sees only pointers, so a tensor of the wrong size would be read or written out
+    of bounds on the GPU; every tensor is checked here before anything is launched."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the device of q)")
+
+
+def _token_inputs(q, k, v, g, beta, name_g="g"):
+    """Shapes of [B, T, H, .] token inputs (q first), checked against each other."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, T, H, dk]")
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, H, dv]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    _expect(k, "k", (B, T, H, dk), dt, dev)
+    _expect(v, "v", (B, T, H, dv), dt, dev)
+    _expect(g, name_g, (B, T, H, dk), dt, dev)
+    _expect(beta, "beta", (B, T, H), dt, dev)
+    return B, T, H, dk, dv
+
+
+def _workspace_bytes(workspace, device) -> int:
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError(f"workspace must be a tensor on {device}")
+    return workspace.numel() * workspace.element_size()
+
+
 def _stream(stream) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -141,25 +179,34 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
     size the library asks for is allocated when not given.  ``gate_logits=True``
     passes raw decay logits in ``g`` (kda_chunk_fwd_gate_logits; log-decay = -softplus).
     """
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    in_dt = q.dtype
-    out_dt = in_dt if out_dtype is None else out_dtype
+    B, T, H, dk, dv = _token_inputs(q, k, v, g, beta)
+    in_dt, dev = q.dtype, q.device
+    out_dt = (o.dtype if o is not None else in_dt) if out_dtype is None else out_dtype
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=out_dt, device=q.device)
+        o = torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+    _expect(o, "o", (B, T, H, dv), out_dt, dev)
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
     if final_state is None and want_final_state:
-        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _expect(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
     if checkpoint_every and checkpoints is None:
         checkpoints = torch.empty((B, T // checkpoint_every, H, dk, dv), dtype=torch.float32,
-                                  device=q.device)
+                                  device=dev)
+    if checkpoints is not None:
+        if not checkpoint_every:
+            raise ValueError("checkpoints given with checkpoint_every = 0")
+        _expect(checkpoints, "checkpoints", (B, T // checkpoint_every, H, dk, dv),
+                torch.float32, dev)
     if segment_tokens is None:
         need = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, in_dt)
     else:
         need = kda_chunk_fwd_segmented_workspace_bytes(B, T, H, dk, dv, segment_tokens, chunk,
                                                        in_dt)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = _workspace_bytes(workspace, dev)
     lib = load_library()
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
             _ptr(final_state), _ptr(checkpoints), int(checkpoint_every), B, T, H, dk, dv, chunk,
@@ -183,11 +230,21 @@ def kda_recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, o=None, strea
                        gate_logits: bool = False):
     """One decode step; ``state`` [N,H,dk,dv] float32 is updated in place.  Returns o [N,H,dv].
     ``gate_logits=True`` passes raw decay logits in ``g``."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or not isinstance(v, torch.Tensor) \
+            or v.dim() != 3:
+        raise ValueError("q and v must be 3-D tensors [N, H, d]")
     N, H, dk = q.shape
     dv = v.shape[-1]
-    out_dt = q.dtype if out_dtype is None else out_dtype
+    dt, dev = q.dtype, q.device
+    _expect(k, "k", (N, H, dk), dt, dev)
+    _expect(v, "v", (N, H, dv), dt, dev)
+    _expect(g, "g", (N, H, dk), dt, dev)
+    _expect(beta, "beta", (N, H), dt, dev)
+    _expect(state, "state", (N, H, dk, dv), torch.float32, dev)
+    out_dt = (o.dtype if o is not None else dt) if out_dtype is None else out_dtype
     if o is None:
-        o = torch.empty((N, H, dv), dtype=out_dt, device=q.device)
+        o = torch.empty((N, H, dv), dtype=out_dt, device=dev)
+    _expect(o, "o", (N, H, dv), out_dt, dev)
     lib = load_library()
     fn = lib.kda_recurrent_step_gate_logits if gate_logits else lib.kda_recurrent_step
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, dk, dv,
@@ -202,11 +259,13 @@ def kda_recurrent_verify(q, k, v, g, beta, state, *, out_dtype=None, o=None, str
 
     q, k, g [N,K,H,dk]; v [N,K,H,dv]; beta [N,K,H]; state [N,H,dk,dv] float32.
     Returns o [N,K,H,dv]."""
-    N, K, H, dk = q.shape
-    dv = v.shape[-1]
-    out_dt = q.dtype if out_dtype is None else out_dtype
+    N, K, H, dk, dv = _token_inputs(q, k, v, g, beta)
+    dev = q.device
+    _expect(state, "state", (N, H, dk, dv), torch.float32, dev)
+    out_dt = (o.dtype if o is not None else q.dtype) if out_dtype is None else out_dtype
     if o is None:
-        o = torch.empty((N, K, H, dv), dtype=out_dt, device=q.device)
+        o = torch.empty((N, K, H, dv), dtype=out_dt, device=dev)
+    _expect(o, "o", (N, K, H, dv), out_dt, dev)
     st = load_library().kda_recurrent_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                              _ptr(state), _ptr(o), N, K, H, dk, dv,
                                              _dtype_code(q.dtype), _dtype_code(o.dtype),
@@ -218,10 +277,17 @@ def kda_recurrent_verify(q, k, v, g, beta, state, *, out_dtype=None, o=None, str
 
 def kda_recurrent_commit(k, v, g, beta, accept, state, *, stream=None):
     """Advance ``state`` [N,H,dk,dv] in place by accept[n] (int32, on the GPU) draft tokens."""
+    if not isinstance(k, torch.Tensor) or k.dim() != 4 or not isinstance(v, torch.Tensor) \
+            or v.dim() != 4:
+        raise ValueError("k and v must be 4-D tensors [N, K, H, d]")
     N, K, H, dk = k.shape
     dv = v.shape[-1]
-    if accept.dtype != torch.int32:
-        raise TypeError("accept must be int32")
+    dt, dev = k.dtype, k.device
+    _expect(v, "v", (N, K, H, dv), dt, dev)
+    _expect(g, "g", (N, K, H, dk), dt, dev)
+    _expect(beta, "beta", (N, K, H), dt, dev)
+    _expect(accept, "accept", (N,), torch.int32, dev)
+    _expect(state, "state", (N, H, dk, dv), torch.float32, dev)
     st = load_library().kda_recurrent_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(accept),
                                              _ptr(state), N, K, H, dk, dv, _dtype_code(k.dtype),
                                              _stream(stream))
@@ -235,22 +301,28 @@ def kda_chunk_fwd_checkpoints_at(q, k, v, g, beta, positions, initial_state=None
                                  chunk: int = 64, workspace=None, stream=None):
     """Chunked forward saving the state after each of ``positions`` tokens (int64 on the GPU,
     increasing multiples of ``chunk``).  Returns (o, final_state, checkpoints [B,P,H,dk,dv])."""
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    B, T, H, dk, dv = _token_inputs(q, k, v, g, beta)
+    dev = q.device
+    if not isinstance(positions, torch.Tensor) or positions.dim() != 1:
+        raise ValueError("positions must be a 1-D tensor")
     P = positions.numel()
-    if positions.dtype != torch.int64:
-        raise TypeError("positions must be int64")
-    out_dt = q.dtype if out_dtype is None else out_dtype
+    _expect(positions, "positions", (P,), torch.int64, dev)
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
+    out_dt = (o.dtype if o is not None else q.dtype) if out_dtype is None else out_dtype
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=out_dt, device=q.device)
+        o = torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+    _expect(o, "o", (B, T, H, dv), out_dt, dev)
     if final_state is None:
-        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _expect(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
     if checkpoints is None:
-        checkpoints = torch.empty((B, P, H, dk, dv), dtype=torch.float32, device=q.device)
+        checkpoints = torch.empty((B, P, H, dk, dv), dtype=torch.float32, device=dev)
+    _expect(checkpoints, "checkpoints", (B, P, H, dk, dv), torch.float32, dev)
     need = kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, q.dtype)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = _workspace_bytes(workspace, dev)
     st = load_library().kda_chunk_fwd_checkpoints_at(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
         _ptr(final_state), _ptr(checkpoints), _ptr(positions), P, B, T, H, dk, dv, chunk,

@@ -57,11 +57,19 @@ constexpr int64_t kChunk = 64;
 // workgroups takes ceil(n / kCUs) rounds.
 constexpr int64_t kCUs = 256;
 
+// The prefill kernel addresses one chunk's token rows as 32-bit byte offsets from the
+// chunk's first row, row * H * d * element size (inputs, and the output in either
+// dtype).  Sizes whose largest such offset does not fit 32 bits are rejected: H at most
+// 131,071 for d = 128 (float32 output), far beyond any model's head count.
+constexpr int64_t kMaxChunkSpanBytes = 0xffffffffLL;
+
 bool sizes_ok(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk, kda_dtype_t in) {
   if (!dtype_ok(in) || B < 1 || T < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv) ||
       chunk != kChunk)
     return false;
   if (in == KDA_F32 && (dk != 64 || dv != 64)) return false;
+  const int64_t dmax = dk > dv ? dk : dv;
+  if (H > kMaxChunkSpanBytes / (kChunk * dmax * 4)) return false;
   return mul_ok(B, T) && mul_ok(B * T, H) && mul_ok(B * T * H, 128);
 }
 

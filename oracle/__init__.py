@@ -39,6 +39,12 @@ from .kda import (  # noqa: F401
     kda_decode_step,
     kda_forward,
     kda_forward_heads_parallel,
+    head_pool,
+    set_default_pool,
+    oracle_processes,
+    apply_output_gate,
+    rel_l2_groups,
+    rel_l2_chunks,
     one_hot_key_rows,
     rel_l2,
 )

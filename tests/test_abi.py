@@ -91,6 +91,11 @@ def test_chunk_fwd_rejects_before_launch(lib):
     assert _fwd(lib, o=2 * FAKE + 64) == -6  # o inside k
     assert _fwd(lib, o=o, sf=o + 128) == -6  # final state overlaps o
     assert _fwd(lib, o=o, s0=80 * FAKE, sf=80 * FAKE + 16) == -6  # partial state overlap
+    # per-chunk row offsets are 32-bit: 64 rows x H x 128 channels x 4 bytes must fit
+    assert _fwd(lib, o=o, H=131072) == -2
+    assert _fwd(lib, o=o, H=262144, dk=64, dv=64) == -2
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 64, 131072, 128, 128, 64, kda.KDA_BF16) == 0
+    assert lib.kda_chunk_fwd_segment_tokens(1, 64, 131072, 128, 128, 64, kda.KDA_BF16) == 0
 
 
 def _seg(lib, seg, ws=None, ws_bytes=0, **kw):
@@ -194,3 +199,50 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 128)
     with pytest.raises((ValueError, RuntimeError)):
         kda.kda_recurrent_step(x, x, x, x, torch.zeros(1, 1), torch.zeros(1, 1, 128, 128))
+
+
+def test_binding_checks_every_tensor_before_launch():
+    """The binding checks shapes, dtypes and devices of every tensor (the C ABI sees only
+    pointers); each bad call raises before any pointer reaches the library."""
+    import torch
+
+    def t(*shape, dtype=torch.bfloat16):
+        return torch.zeros(*shape, dtype=dtype)
+
+    B, T, H, d = 1, 8, 2, 64
+    q, k, v, g, beta = t(B, T, H, d), t(B, T, H, d), t(B, T, H, d), t(B, T, H, d), t(B, T, H)
+    bad = [
+        dict(k=t(B, T, H, d + 1)),                       # k of another size
+        dict(k=t(B, T, H, d, dtype=torch.float32)),       # k of another dtype
+        dict(g=t(B, T + 1, H, d)),
+        dict(beta=t(B, T, H, 1)),
+        dict(v=t(B, T, H + 1, d)),
+        dict(initial_state=t(B, H, d, d)),                # state must be float32
+        dict(initial_state=t(B, H, d, d - 1, dtype=torch.float32)),
+        dict(o=t(B, T, H, d - 1)),
+        dict(final_state=t(B, H, d, d, dtype=torch.float32)[:, :1]),
+        dict(checkpoints=t(B, 1, H, d, d, dtype=torch.float32)),  # given without every
+        dict(workspace=[0] * 16),
+    ]
+    for kw in bad:
+        args = dict(q=q, k=k, v=v, g=g, beta=beta)
+        args.update({n: kw[n] for n in ("k", "v", "g", "beta") if n in kw})
+        rest = {n: x for n, x in kw.items() if n not in ("k", "v", "g", "beta")}
+        with pytest.raises((ValueError, TypeError)):
+            kda.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], **rest)
+    st = t(B, H, d, d, dtype=torch.float32)
+    q1, v1, b1 = t(B, H, d), t(B, H, d), t(B, H)
+    for kw in [dict(k=t(B, H, d + 1)), dict(beta=t(B, H, 2)), dict(state=t(B, H, d, d)),
+               dict(state=t(B, H + 1, d, d, dtype=torch.float32)), dict(o=t(B, H, d - 1))]:
+        a = dict(q=q1, k=q1, v=v1, g=q1, beta=b1, state=st)
+        a.update(kw)
+        o = a.pop("o", None)
+        with pytest.raises((ValueError, TypeError)):
+            kda.kda_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], o=o)
+    acc = torch.zeros(B, dtype=torch.int64)  # must be int32
+    with pytest.raises((ValueError, TypeError)):
+        kda.kda_recurrent_commit(k, v, g, beta, acc, st)
+    with pytest.raises((ValueError, TypeError)):
+        kda.kda_recurrent_verify(q, k, v, g, beta, t(B, H, d, d, dtype=torch.float32)[:, :1])
+    with pytest.raises((ValueError, TypeError)):
+        kda.kda_chunk_fwd_checkpoints_at(q, k, v, g, beta, torch.zeros(2, dtype=torch.int32))

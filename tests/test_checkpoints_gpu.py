@@ -8,6 +8,7 @@ import torch
 
 import gated_delta_rule_57_amd as kda
 import oracle
+import parity
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -40,9 +41,9 @@ def test_listed_positions_match_oracle(B, T, H, positions):
     torch.cuda.synchronize()
     o_r, s_r, ck_r = _oracle_chunk_states(x)
     want = ck_r[:, [p // 64 - 1 for p in positions]]
-    e_c, e_o = oracle.rel_l2(_np(ck), want), oracle.rel_l2(_np(o), o_r)
-    print(f"[ckpt] B{B} T{T} H{H} segment {seg}: checkpoints {e_c:.3e} o {e_o:.3e}", flush=True)
-    assert e_c <= 3e-3 and e_o <= 3e-3
+    print(f"[ckpt] B{B} T{T} H{H} segment {seg}", flush=True)
+    parity.check("checkpoints", ck, want, 3e-3, "ckpt")
+    parity.check("o", o, o_r, 3e-3, "tokens")
     if positions[-1] == T:
         assert torch.equal(ck[:, -1], sf)
 
@@ -59,7 +60,7 @@ def test_entries_off_chunk_ends_are_untouched():
     torch.cuda.synchronize()
     assert torch.isnan(ck[:, [0, 2, 3]]).all()
     _, _, ck_r = _oracle_chunk_states(x)
-    assert oracle.rel_l2(_np(ck[:, 1]), ck_r[:, 256 // 64 - 1]) <= 3e-3
+    parity.check("checkpoint after 256 tokens", ck[:, 1], ck_r[:, 256 // 64 - 1], 3e-3, "state")
 
 
 def test_restoring_a_checkpoint_continues_the_sequence():
@@ -77,7 +78,7 @@ def test_restoring_a_checkpoint_continues_the_sequence():
                                   ck[:, 0].contiguous(), out_dtype=torch.float32)
     torch.cuda.synchronize()
     o_r, s_r, _ = _oracle_chunk_states(x)
-    e_o, e_s = oracle.rel_l2(_np(o2), o_r[:, 512:]), oracle.rel_l2(_np(s2), s_r)
-    print(f"[ckpt] restored at 512: o {e_o:.3e} state {e_s:.3e}", flush=True)
-    assert e_o <= 3e-3 and e_s <= 3e-3
+    print("[ckpt] restored at 512", flush=True)
+    parity.check("o after the restore", o2, o_r[:, 512:], 3e-3, "tokens")
+    parity.check("final state", s2, s_r, 3e-3, "state")
     assert oracle.rel_l2(_np(o2), _np(o[:, 512:])) <= 1e-3

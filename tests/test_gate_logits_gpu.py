@@ -7,6 +7,7 @@ import torch
 
 import gated_delta_rule_57_amd as kda
 import oracle
+import parity
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -34,9 +35,9 @@ def test_prefill_from_logits_matches_oracle(w):
     o, s, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["beta"], d["s0"],
                                 out_dtype=torch.float32, gate_logits=True)
     torch.cuda.synchronize()
-    e_o, e_s = oracle.rel_l2(_np(o), o_r), oracle.rel_l2(_np(s), s_r)
-    print(f"[logits] {w.name} {w.dtype} T{w.T}: o {e_o:.3e} state {e_s:.3e}", flush=True)
-    assert e_o <= TOL[w.dtype] and e_s <= TOL[w.dtype]
+    print(f"[logits] {w.name} {w.dtype} T{w.T}", flush=True)
+    parity.check("o", o, o_r, TOL[w.dtype], "tokens")
+    parity.check("final state", s, s_r, TOL[w.dtype], "state")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -55,10 +56,8 @@ def test_decode_from_logits_matches_oracle(dtype):
         o_r, S = oracle.kda_decode_step(S, x["q"][:, t], x["k"][:, t], x["v"][:, t],
                                         oracle.log_decay_from_logits(x["a"][:, t]), x["beta"][:, t])
         torch.cuda.synchronize()
-        assert oracle.rel_l2(_np(o), o_r) <= TOL[dtype]
-    e_s = oracle.rel_l2(_np(state), S)
-    print(f"[logits] decode {dtype}: state {e_s:.3e}", flush=True)
-    assert e_s <= TOL[dtype]
+        parity.check(f"decode o, token {t}", o, o_r, TOL[dtype], "step")
+    parity.check(f"decode {dtype} state", state, S, TOL[dtype], "state")
 
 
 def test_nan_logit_stays_in_its_head():

@@ -7,6 +7,7 @@ import torch
 
 import gated_delta_rule_57_amd as kda
 import oracle
+import parity
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -116,8 +117,8 @@ def test_decode_steps_equal_prefill(dtype):
     torch.cuda.synchronize()
     od = torch.stack(outs, 1)
     tol = 1e-5 if dtype == "f32" else 3e-3
-    assert oracle.rel_l2(od.double().cpu().numpy(), o.double().cpu().numpy()) <= tol
-    assert oracle.rel_l2(st.double().cpu().numpy(), sf.double().cpu().numpy()) <= tol
+    parity.check("decode steps vs prefill o", od, o, tol, "tokens")
+    parity.check("decode steps vs prefill state", st, sf, tol, "state")
 
 
 def _w(dtype, T=300, H=3):

@@ -297,9 +297,12 @@ def test_heads_parallel_matches_batched():
     beta = rng.uniform(0, 1, (B, T, H))
     s0 = rng.standard_normal((B, H, dk, dv))
     ref = oracle.kda_forward(q, k, v, g, beta, s0, 7)
-    (o, S, ck), n = oracle.kda_forward_heads_parallel(q, k, v, g, beta, s0, 7, processes=2)
-    assert n == 2
-    assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1]) and np.array_equal(ck, ref[2])
+    # a pool of its own, the session's default pool, and in-process
+    for kw in ({"processes": 2}, {}, {"processes": 1}):
+        (o, S, ck), n = oracle.kda_forward_heads_parallel(q, k, v, g, beta, s0, 7, **kw)
+        assert n == kw.get("processes", n)
+        assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1])
+        assert np.array_equal(ck, ref[2])
 
 
 # ---------------------------------------------------------------- mutation check
@@ -394,3 +397,139 @@ def test_negative_softplus_closed_forms():
     g = f(np.linspace(-20.0, 20.0, 401))
     assert np.all(np.diff(g) < 0) and np.all(g < 0)
     assert oracle.clamp_log_decay(f(np.log(np.expm1(5.0)))) == pytest.approx(-5.0, abs=1e-14)
+
+
+# ------------------------------------------------------------- comparators
+# Every parity claim is a value of these functions, so they are pinned by hand values
+# and by copies with plausible mistakes planted in them, not by re-evaluating them.
+
+
+def _rel_no_sqrt(x, ref):
+    x, ref = np.asarray(x, float), np.asarray(ref, float)
+    return float(np.sum((x - ref) ** 2) / np.sum(ref ** 2))
+
+
+def _rel_wrong_denominator(x, ref):
+    x, ref = np.asarray(x, float), np.asarray(ref, float)
+    return float(np.linalg.norm(x - ref) / np.linalg.norm(x))
+
+
+def _rel_max_abs(x, ref):
+    x, ref = np.asarray(x, float), np.asarray(ref, float)
+    return float(np.max(np.abs(x - ref)) / np.linalg.norm(ref))
+
+
+def _rel_l1(x, ref):
+    x, ref = np.asarray(x, float), np.asarray(ref, float)
+    return float(np.sum(np.abs(x - ref)) / np.sum(np.abs(ref)))
+
+
+# (x, ref, value worked out by hand)
+REL_L2_HAND = [
+    # x - ref = [1, 2, -2]: norm 3; ||ref|| = 4
+    ([1.0, 2.0, 2.0], [0.0, 0.0, 4.0], 0.75),
+    # x - ref = [3, -1]: norm sqrt(10); ||ref|| = 5
+    ([3.0, 4.0], [0.0, 5.0], math.sqrt(10.0) / 5.0),
+    # equal arrays, in any shape
+    ([[1.5, -2.0], [0.25, 8.0]], [[1.5, -2.0], [0.25, 8.0]], 0.0),
+    # zero in place of ref: the whole of ref is missing
+    ([0.0, 0.0, 0.0, 0.0], [1.0, -1.0, 1.0, -1.0], 1.0),
+    # 2x ref: off by ref itself
+    ([2.0, -6.0], [1.0, -3.0], 1.0),
+    # ref all zeros: the plain norm of x (documented special case)
+    ([3.0, 4.0], [0.0, 0.0], 5.0),
+]
+
+
+@pytest.mark.parametrize("x,ref,want", REL_L2_HAND)
+def test_rel_l2_hand_values(x, ref, want):
+    assert oracle.rel_l2(np.array(x), np.array(ref)) == pytest.approx(want, rel=1e-15, abs=1e-300)
+
+
+@pytest.mark.parametrize("mistake", [_rel_no_sqrt, _rel_wrong_denominator, _rel_max_abs, _rel_l1],
+                         ids=lambda f: f.__name__)
+def test_rel_l2_hand_values_reject_planted_mistakes(mistake):
+    """Each plausible mistake in the comparator misses at least one hand value."""
+    wrong = 0
+    for x, ref, want in REL_L2_HAND[:2]:
+        with np.errstate(all="ignore"):
+            got = mistake(np.array(x), np.array(ref))
+        wrong += abs(got - want) > 1e-9
+    assert wrong > 0
+
+
+def test_rel_l2_groups_hand_values():
+    # two heads (axis 2) of a [1, 2, 2, 2] output: head 0 exact, head 1 off by [1, 2, -2] / 4
+    ref = np.zeros((1, 2, 2, 2))
+    ref[0, :, 0] = [[1.0, 2.0], [3.0, 4.0]]
+    ref[0, :, 1] = [[0.0, 0.0], [0.0, 4.0]]
+    x = ref.copy()
+    x[0, :, 1] = [[1.0, 2.0], [0.0, 2.0]]
+    per = oracle.rel_l2_groups(x, ref, (0, 2))
+    assert per.shape == (1, 2)
+    assert per[0, 0] == 0.0 and per[0, 1] == pytest.approx(0.75, rel=1e-15)
+    # the whole-tensor value mixes both heads: sqrt(9 / (30 + 16))
+    assert oracle.rel_l2(x, ref) == pytest.approx(3.0 / math.sqrt(46.0), rel=1e-15)
+    # states [B, H, dk, dv]: one value per (b, h)
+    s_ref = np.ones((2, 3, 2, 2))
+    s = s_ref.copy()
+    s[1, 2, 0, 0] = 3.0  # off by 2 in one of four unit entries: 2 / 2
+    per_s = oracle.rel_l2_groups(s, s_ref, (0, 1))
+    assert per_s.shape == (2, 3) and per_s[1, 2] == pytest.approx(1.0) and per_s.sum() == per_s[1, 2]
+
+
+def test_rel_l2_chunks_hand_values():
+    # one head, T = 5 tokens, D = 1, chunks of 2: token runs [0, 1], [2, 3], [4]
+    ref = np.array([3.0, 4.0, 1.0, 0.0, 2.0]).reshape(1, 5, 1, 1)
+    x = np.array([3.0, 4.0, 1.0, 1.0, 1.0]).reshape(1, 5, 1, 1)
+    per = oracle.rel_l2_chunks(x, ref, 2)
+    assert per.shape == (1, 3, 1)
+    assert per[0, 0, 0] == 0.0
+    assert per[0, 1, 0] == pytest.approx(1.0)        # |[0, 1]| / |[1, 0]|
+    assert per[0, 2, 0] == pytest.approx(0.5)        # the one-token tail: 1 / 2
+    # chunks of the whole length reduce to the per-head value
+    assert oracle.rel_l2_chunks(x, ref, 5)[0, 0, 0] == pytest.approx(
+        oracle.rel_l2_groups(x, ref, (0, 2))[0, 0])
+
+
+def test_one_wrong_token_head_hides_in_the_whole_tensor_but_not_per_head_or_chunk():
+    """Why the parity helpers assert maxima too: at the 4 x 4096 x 32-head size, one
+    token-head gone completely wrong moves the whole-tensor error by only about 1.4e-3,
+    under the 3e-3 bound; the per-head and per-chunk maxima see it at once."""
+    rng = np.random.default_rng(5)
+    ref = rng.standard_normal((2, 256, 8, 16))
+    x = ref * (1.0 + 1e-4 * rng.standard_normal(ref.shape))
+    x[1, 200, 3] = rng.standard_normal(16)  # one token of one head replaced
+    assert oracle.rel_l2(x, ref) < 3e-2
+    assert oracle.rel_l2_groups(x, ref, (0, 2)).max() > 5e-2
+    per_chunk = oracle.rel_l2_chunks(x, ref, 64)
+    assert per_chunk.max() > 1e-1 and np.argwhere(per_chunk > 1e-2).tolist() == [[1, 3, 3]]
+
+
+# ------------------------------------------------------------- output gate
+
+
+def test_output_gate_closed_forms():
+    """o * sigmoid(z): pinned by values of the logistic function that need no evaluation
+    of it (z = 0, z = log 3, the tails, the symmetry sigma(z) + sigma(-z) = 1)."""
+    f = oracle.apply_output_gate
+    o = np.array([2.0, -4.0, 8.0, 1.0])
+    assert np.array_equal(f(o, np.zeros(4)), o / 2.0)
+    # sigma(log 3) = 3 / 4, sigma(-log 3) = 1 / 4
+    assert f(o, np.full(4, np.log(3.0))) == pytest.approx(0.75 * o, rel=1e-15)
+    assert f(o, np.full(4, -np.log(3.0))) == pytest.approx(0.25 * o, rel=1e-15)
+    # saturation: +inf passes o through, -inf closes the gate; no overflow on the way
+    with np.errstate(all="raise"):
+        assert np.array_equal(f(o, np.full(4, np.inf)), o)
+        assert np.array_equal(f(o, np.full(4, -np.inf)), 0.0 * o)
+        assert np.array_equal(f(o, np.full(4, 800.0)), o)
+        assert np.all(f(o, np.full(4, -800.0)) == 0.0)
+    z = np.linspace(-30.0, 30.0, 121)
+    one = np.ones_like(z)
+    assert np.allclose(f(one, z) + f(one, -z), 1.0, rtol=0, atol=1e-15)
+    # its derivative at 0 is 1/4; monotone; gates each element by its own z
+    h = 1e-6
+    assert (f(1.0, h) - f(1.0, -h)) / (2 * h) == pytest.approx(0.25, rel=1e-8)
+    assert np.all(np.diff(f(one, z)) > 0)
+    assert np.array_equal(f(o, np.array([np.inf, -np.inf, 0.0, np.inf])), [2.0, -0.0, 4.0, 1.0])
+    assert np.isnan(f(o, np.array([np.nan, 0, 0, 0]))[0])

@@ -5,6 +5,7 @@ import torch
 
 import gated_delta_rule_57_amd as kda
 import oracle
+import parity
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -33,12 +34,11 @@ def _check(w, out_dtype=None, every=0, tol=None, x=None):
           f"out={out_dtype}", flush=True)
     o, s, ck = _gpu(w, x, out_dtype, every)
     o_r, s_r, ck_r = _ref(x, every)
-    e_o, e_s = oracle.rel_l2(o, o_r), oracle.rel_l2(s, s_r)
-    print(f"[prefill]   rel_l2 o {e_o:.3e} state {e_s:.3e}", flush=True)
     tol = TOL[w.dtype] if tol is None else tol
-    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+    e_o = parity.check("o", o, o_r, tol, "tokens")
+    e_s = parity.check("final state", s, s_r, tol, "state")
     if every:
-        assert oracle.rel_l2(ck, ck_r) <= tol
+        parity.check("checkpoints", ck, ck_r, tol, "ckpt")
     return e_o, e_s
 
 
@@ -121,10 +121,9 @@ def test_million_token_prefix_checkpoint():
     x = {n: d[n][:, :P].double().cpu().numpy() for n in ("q", "k", "v", "g", "beta")}
     s0 = d["s0"].double().cpu().numpy()
     o_r, s_r, _ = _ref(dict(x, s0=s0))
-    e_o = oracle.rel_l2(o[:, :P].double().cpu().numpy(), o_r)
-    e_s = oracle.rel_l2(ck[:, 0].double().cpu().numpy(), s_r)
-    print(f"[prefill] 1M tokens, prefix {P}: o {e_o:.3e} checkpoint {e_s:.3e}", flush=True)
-    assert e_o <= 3e-3 and e_s <= 3e-3
+    print(f"[prefill] 1M tokens, prefix {P}", flush=True)
+    parity.check("o over the prefix", o[:, :P], o_r, 3e-3, "tokens")
+    parity.check("checkpoint after the prefix", ck[:, 0], s_r, 3e-3, "state")
     assert bool(torch.isfinite(sf).all()) and bool(torch.isfinite(o.float()).all())
     # the last checkpoint is the final state
     assert torch.equal(ck[:, -1], sf)

@@ -7,6 +7,7 @@ import torch
 
 import gated_delta_rule_57_amd as kda
 import oracle
+import parity
 import synth
 
 pytestmark = pytest.mark.gpu
@@ -45,14 +46,11 @@ def _check(w, seg, out_dtype=None, every=0, tol=None):
     o, s, ck = _run(d, seg, out_dtype=out_dtype, checkpoint_every=every)
     torch.cuda.synchronize()
     o_r, s_r, ck_r = _ref(x, every)
-    e_o, e_s = oracle.rel_l2(_np(o), o_r), oracle.rel_l2(_np(s), s_r)
-    print(f"[segments]   rel_l2 o {e_o:.3e} state {e_s:.3e}", flush=True)
     tol = TOL[w.dtype] if tol is None else tol
-    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+    parity.check("o", o, o_r, tol, "tokens")
+    parity.check("final state", s, s_r, tol, "state")
     if every:
-        e_c = oracle.rel_l2(_np(ck), ck_r)
-        print(f"[segments]   checkpoints {e_c:.3e}", flush=True)
-        assert e_c <= tol
+        parity.check("checkpoints", ck, ck_r, tol, "ckpt")
     return o, s
 
 
@@ -98,11 +96,11 @@ def test_bf16_long_memory_segments_vs_one_pass():
     o2, s2, _ = _run(d, 1024, out_dtype=torch.float32)
     torch.cuda.synchronize()
     o_r, s_r, _ = _ref(x)
-    e1 = (oracle.rel_l2(_np(o1), o_r), oracle.rel_l2(_np(s1), s_r))
-    e2 = (oracle.rel_l2(_np(o2), o_r), oracle.rel_l2(_np(s2), s_r))
-    print(f"[segments] long memory: one pass o {e1[0]:.3e} state {e1[1]:.3e}; "
-          f"5 segments o {e2[0]:.3e} state {e2[1]:.3e}", flush=True)
-    assert max(e1 + e2) <= LONG_MEMORY_TOL
+    print("[segments] long memory, one pass and 5 segments", flush=True)
+    e1 = (parity.check("one pass o", o1, o_r, LONG_MEMORY_TOL, "tokens"),
+          parity.check("one pass state", s1, s_r, LONG_MEMORY_TOL, "state"))
+    e2 = (parity.check("5 segments o", o2, o_r, LONG_MEMORY_TOL, "tokens"),
+          parity.check("5 segments state", s2, s_r, LONG_MEMORY_TOL, "state"))
     # cutting the sequence adds no error of its own beyond rounding-order noise
     assert e2[0] <= 1.25 * e1[0] and e2[1] <= 1.25 * e1[1]
 
@@ -156,6 +154,6 @@ def test_library_choice_of_segments_for_few_heads():
     o, s, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
     torch.cuda.synchronize()
     o_r, s_r, _ = _ref(x)
-    e_o, e_s = oracle.rel_l2(_np(o), o_r), oracle.rel_l2(_np(s), s_r)
-    print(f"[segments] library choice {seg}: o {e_o:.3e} state {e_s:.3e}", flush=True)
-    assert e_o <= 3e-3 and e_s <= 3e-3
+    print(f"[segments] library choice {seg}", flush=True)
+    parity.check("o", o, o_r, 3e-3, "tokens")
+    parity.check("final state", s, s_r, 3e-3, "state")
