@@ -23,7 +23,8 @@ EXPORTS = ("kda_status_str", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_bytes",
            "kda_chunk_fwd_segment_tokens", "kda_chunk_fwd_checkpoints_at", "kda_recurrent_step",
            "kda_recurrent_verify", "kda_recurrent_commit", "kda_chunk_fwd_gate_logits",
-           "kda_recurrent_step_gate_logits")
+           "kda_recurrent_step_gate_logits", "kda_chunk_fwd_output_gate",
+           "kda_recurrent_step_output_gate")
 
 _lib = None
 
@@ -69,6 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_gate_logits.argtypes = list(lib.kda_chunk_fwd.argtypes)
     lib.kda_recurrent_step_gate_logits.restype = c_int
     lib.kda_recurrent_step_gate_logits.argtypes = list(lib.kda_recurrent_step.argtypes)
+    lib.kda_chunk_fwd_output_gate.restype = c_int
+    lib.kda_chunk_fwd_output_gate.argtypes = [vp] * 6 + list(lib.kda_chunk_fwd.argtypes[5:])
+    lib.kda_recurrent_step_output_gate.restype = c_int
+    lib.kda_recurrent_step_output_gate.argtypes = [vp] * 6 + list(lib.kda_recurrent_step.argtypes[5:])
     lib.kda_recurrent_verify.restype = c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int,
                                          c_int, c_int, vp]
@@ -168,7 +173,8 @@ def kda_chunk_fwd_segment_tokens(B: int, T: int, H: int, dk: int, dv: int, chunk
 def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=None,
                   final_state=None, want_final_state=True, checkpoint_every: int = 0,
                   checkpoints=None, chunk: int = 64, workspace=None, stream=None,
-                  segment_tokens: Optional[int] = None, gate_logits: bool = False):
+                  segment_tokens: Optional[int] = None, gate_logits: bool = False,
+                  output_gate=None):
     """Chunked KDA forward.  Shapes as in include/kda.h; returns (o, final_state, checkpoints).
 
     q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (all one dtype); initial_state
@@ -178,6 +184,8 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
     calls kda_chunk_fwd_segmented with that segment length.  A workspace of the
     size the library asks for is allocated when not given.  ``gate_logits=True``
     passes raw decay logits in ``g`` (kda_chunk_fwd_gate_logits; log-decay = -softplus).
+    ``output_gate`` [B,T,H,dv] (q's dtype) calls kda_chunk_fwd_output_gate: o = (S^T q) *
+    sigmoid(output_gate).
     """
     B, T, H, dk, dv = _token_inputs(q, k, v, g, beta)
     in_dt, dev = q.dtype, q.device
@@ -212,7 +220,13 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
             _ptr(final_state), _ptr(checkpoints), int(checkpoint_every), B, T, H, dk, dv, chunk,
             _dtype_code(in_dt), _dtype_code(o.dtype))
     tail = (_ptr(workspace), ws_bytes, _stream(stream))
-    if gate_logits:
+    if output_gate is not None:
+        _expect(output_gate, "output_gate", (B, T, H, dv), in_dt, dev)
+        if gate_logits or segment_tokens is not None:
+            raise ValueError("output_gate takes log-decays and the library's segmentation")
+        st = lib.kda_chunk_fwd_output_gate(*args[:5], _ptr(output_gate), *args[5:], *tail)
+        where = "kda_chunk_fwd_output_gate"
+    elif gate_logits:
         if segment_tokens is not None:
             raise ValueError("gate_logits takes the library's segmentation")
         st, where = lib.kda_chunk_fwd_gate_logits(*args, *tail), "kda_chunk_fwd_gate_logits"
@@ -227,9 +241,10 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, *, out_dtype=None, o=Non
 
 
 def kda_recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, o=None, stream=None,
-                       gate_logits: bool = False):
+                       gate_logits: bool = False, output_gate=None):
     """One decode step; ``state`` [N,H,dk,dv] float32 is updated in place.  Returns o [N,H,dv].
-    ``gate_logits=True`` passes raw decay logits in ``g``."""
+    ``gate_logits=True`` passes raw decay logits in ``g``; ``output_gate`` [N,H,dv] gives
+    o = (S^T q) * sigmoid(output_gate)."""
     if not isinstance(q, torch.Tensor) or q.dim() != 3 or not isinstance(v, torch.Tensor) \
             or v.dim() != 3:
         raise ValueError("q and v must be 3-D tensors [N, H, d]")
@@ -246,9 +261,17 @@ def kda_recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, o=None, strea
         o = torch.empty((N, H, dv), dtype=out_dt, device=dev)
     _expect(o, "o", (N, H, dv), out_dt, dev)
     lib = load_library()
-    fn = lib.kda_recurrent_step_gate_logits if gate_logits else lib.kda_recurrent_step
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, dk, dv,
-            _dtype_code(q.dtype), _dtype_code(o.dtype), _stream(stream))
+    tail = (_ptr(state), _ptr(o), N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(o.dtype),
+            _stream(stream))
+    if output_gate is not None:
+        _expect(output_gate, "output_gate", (N, H, dv), dt, dev)
+        if gate_logits:
+            raise ValueError("output_gate takes log-decays")
+        st = lib.kda_recurrent_step_output_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                                _ptr(output_gate), *tail)
+    else:
+        fn = lib.kda_recurrent_step_gate_logits if gate_logits else lib.kda_recurrent_step
+        st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), *tail)
     if st != 0:
         raise KdaError(st, "kda_recurrent_step")
     return o

@@ -128,7 +128,8 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
                             int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
                             kda_dtype_t in, kda_dtype_t out, int64_t seg_len, void* workspace,
                             size_t workspace_bytes, void* stream, const int64_t* ck_pos = nullptr,
-                            int64_t n_ck = 0, bool gate_logits = false) {
+                            int64_t n_ck = 0, bool gate_logits = false,
+                            const void* ogate = nullptr) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
   if ((checkpoint_every != 0 || n_ck != 0) && !checkpoints) return KDA_ERR_NULL;
   if (n_ck != 0 && !ck_pos) return KDA_ERR_NULL;
@@ -147,7 +148,8 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
   const size_t ws_need = segment_workspace(B, H, nseg, dk, dv, &off_z, &off_p);
   if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
-  const void* ptrs[] = {q, k, v, g, beta, initial_state, o, final_state, checkpoints, workspace};
+  const void* ptrs[] = {q,           k,           v,         g,     beta, initial_state, o,
+                        final_state, checkpoints, workspace, ogate};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
 
@@ -157,9 +159,11 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
   const Span sq = span(q, ntok * dk * es), sk = span(k, ntok * dk * es);
   const Span sv = span(v, ntok * dv * es), sg = span(g, ntok * dk * es);
   const Span sb = span(beta, ntok * es);
+  // the output gate, if any, is one more input (an empty span otherwise)
+  const Span sz = ogate ? span(ogate, ntok * dv * es) : Span{0, 0};
   const Span so = span(o, ntok * dv * esize(out));
   const int64_t state_bytes = heads * dk * dv * 4;
-  const Span inputs[] = {sq, sk, sv, sg, sb};
+  const Span inputs[] = {sq, sk, sv, sg, sb, sz};
   for (const Span& s : inputs)
     if (overlaps(so, s)) return KDA_ERR_ALIAS;
   if (initial_state && overlaps(so, span(initial_state, state_bytes))) return KDA_ERR_ALIAS;
@@ -197,7 +201,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, o, final_state,
                      nck > 0 ? checkpoints : nullptr, B, T, H, checkpoint_every,
                      nseg > 1 ? seg_len : T, nseg, 0, nullptr, nullptr, nullptr,
-                     n_ck > 0 ? ck_pos : nullptr, n_ck, gate_logits ? 1 : 0};
+                     n_ck > 0 ? ck_pos : nullptr, n_ck, gate_logits ? 1 : 0, ogate};
   if (nseg > 1) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* seg_in = reinterpret_cast<float*>(ws);
@@ -270,7 +274,8 @@ extern "C" kda_status_t kda_chunk_fwd_segmented(
 static kda_status_t recurrent_step_impl(const void* q, const void* k, const void* v, const void* g,
                                         const void* beta, float* state, void* o, int64_t N,
                                         int64_t H, int dk, int dv, kda_dtype_t in, kda_dtype_t out,
-                                        void* stream, bool gate_logits) {
+                                        void* stream, bool gate_logits,
+                                        const void* ogate = nullptr) {
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
   if (!dtype_ok(in) || !dtype_ok(out)) return KDA_ERR_DTYPE;
   if (N < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_SHAPE;
@@ -278,18 +283,31 @@ static kda_status_t recurrent_step_impl(const void* q, const void* k, const void
   const void* ptrs[] = {q, k, v, g, beta, state, o};
   for (const void* p : ptrs)
     if (!aligned16(p)) return KDA_ERR_ALIGN;
+  if (ogate && !aligned16(ogate)) return KDA_ERR_ALIGN;
   const int64_t nh = N * H, es = esize(in);
   const Span ss = span(state, nh * dk * dv * 4);
   const Span so = span(o, nh * dv * esize(out));
   const Span inputs[] = {span(q, nh * dk * es), span(k, nh * dk * es), span(v, nh * dv * es),
-                         span(g, nh * dk * es), span(beta, nh * es)};
+                         span(g, nh * dk * es), span(beta, nh * es),
+                         ogate ? span(ogate, nh * dv * es) : Span{0, 0}};
   if (overlaps(so, ss)) return KDA_ERR_ALIAS;
   for (const Span& s : inputs)
     if (overlaps(so, s) || overlaps(ss, s)) return KDA_ERR_ALIAS;
   const hipError_t e = kda::decode_step(q, k, v, g, beta, state, o, nh, dk, dv, in == KDA_BF16,
                                         out == KDA_BF16, reinterpret_cast<hipStream_t>(stream),
-                                        gate_logits);
+                                        gate_logits, ogate);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+extern "C" kda_status_t kda_recurrent_step_output_gate(const void* q, const void* k,
+                                                       const void* v, const void* g,
+                                                       const void* beta, const void* gate,
+                                                       float* state, void* o, int64_t N,
+                                                       int64_t H, int dk, int dv, kda_dtype_t in,
+                                                       kda_dtype_t out, void* stream) {
+  if (!gate) return KDA_ERR_NULL;
+  return recurrent_step_impl(q, k, v, g, beta, state, o, N, H, dk, dv, in, out, stream, false,
+                             gate);
 }
 
 extern "C" kda_status_t kda_recurrent_step(const void* q, const void* k, const void* v,
@@ -388,4 +406,18 @@ extern "C" kda_status_t kda_chunk_fwd_gate_logits(
   return chunk_fwd_impl(q, k, v, a, beta, initial_state, o, final_state, checkpoints,
                         checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
                         workspace_bytes, stream, nullptr, 0, true);
+}
+
+extern "C" kda_status_t kda_chunk_fwd_output_gate(
+    const void* q, const void* k, const void* v, const void* g, const void* beta, const void* gate,
+    const float* initial_state, void* o, float* final_state, float* checkpoints,
+    int64_t checkpoint_every, int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
+    kda_dtype_t in, kda_dtype_t out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate) return KDA_ERR_NULL;
+  const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          : kChunk;
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
+                        checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
+                        workspace_bytes, stream, nullptr, 0, false, gate);
 }

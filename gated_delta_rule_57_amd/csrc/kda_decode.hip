@@ -22,7 +22,7 @@ template <typename TIn, typename TOut, int DK, int DV, bool LOGITS>
 __global__ void __launch_bounds__(256) decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const TIn* __restrict__ g, const TIn* __restrict__ beta, float* __restrict__ state,
-    TOut* __restrict__ o, int64_t n_heads_total) {
+    TOut* __restrict__ o, int64_t n_heads_total, const TIn* __restrict__ ogate) {
   constexpr int NT = 256;
   constexpr int CG = DV / 4;    // column groups of 4 floats
   constexpr int RG = NT / CG;   // row groups
@@ -93,7 +93,9 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
     const float bt = to_f32(beta[hd]);
     const float u = bt * (to_f32(v[hd * DV + t]) - a);
     s_u[t] = u;
-    o[hd * DV + t] = from_f32<TOut>(b + s_kq * u);
+    float ov = b + s_kq * u;
+    if (ogate) ov *= sigmoid_hw(to_f32(ogate[hd * DV + t]));  // output gate, if given
+    o[hd * DV + t] = from_f32<TOut>(ov);
   }
   __syncthreads();
 
@@ -281,29 +283,29 @@ multi_token_kernel(
 template <typename TIn, typename TOut, int DK, int DV, bool LOGITS>
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, float* state, void* o, int64_t nh,
-                         hipStream_t stream) {
+                         const void* ogate, hipStream_t stream) {
   decode_step_kernel<TIn, TOut, DK, DV, LOGITS><<<dim3((unsigned)nh), dim3(256), 0, stream>>>(
       (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, state,
-      (TOut*)o, nh);
+      (TOut*)o, nh, (const TIn*)ogate);
   return hipGetLastError();
 }
 
 template <typename TIn, typename TOut, bool LOGITS>
 hipError_t dispatch_decode_dl(const void* q, const void* k, const void* v, const void* g,
                               const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                              hipStream_t s) {
-  if (dk == 128 && dv == 128) return launch_decode<TIn, TOut, 128, 128, LOGITS>(q, k, v, g, beta, state, o, nh, s);
-  if (dk == 64 && dv == 64) return launch_decode<TIn, TOut, 64, 64, LOGITS>(q, k, v, g, beta, state, o, nh, s);
-  if (dk == 64 && dv == 128) return launch_decode<TIn, TOut, 64, 128, LOGITS>(q, k, v, g, beta, state, o, nh, s);
-  return launch_decode<TIn, TOut, 128, 64, LOGITS>(q, k, v, g, beta, state, o, nh, s);
+                              const void* z, hipStream_t s) {
+  if (dk == 128 && dv == 128) return launch_decode<TIn, TOut, 128, 128, LOGITS>(q, k, v, g, beta, state, o, nh, z, s);
+  if (dk == 64 && dv == 64) return launch_decode<TIn, TOut, 64, 64, LOGITS>(q, k, v, g, beta, state, o, nh, z, s);
+  if (dk == 64 && dv == 128) return launch_decode<TIn, TOut, 64, 128, LOGITS>(q, k, v, g, beta, state, o, nh, z, s);
+  return launch_decode<TIn, TOut, 128, 64, LOGITS>(q, k, v, g, beta, state, o, nh, z, s);
 }
 
 template <typename TIn, typename TOut>
 hipError_t dispatch_decode_d(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                             hipStream_t s, bool gate_logits) {
-  return gate_logits ? dispatch_decode_dl<TIn, TOut, true>(q, k, v, g, beta, state, o, nh, dk, dv, s)
-                     : dispatch_decode_dl<TIn, TOut, false>(q, k, v, g, beta, state, o, nh, dk, dv, s);
+                             hipStream_t s, bool gate_logits, const void* z) {
+  return gate_logits ? dispatch_decode_dl<TIn, TOut, true>(q, k, v, g, beta, state, o, nh, dk, dv, z, s)
+                     : dispatch_decode_dl<TIn, TOut, false>(q, k, v, g, beta, state, o, nh, dk, dv, z, s);
 }
 
 template <typename TIn, typename TOut, bool COMMIT>
@@ -341,14 +343,15 @@ hipError_t multi_token(const void* q, const void* k, const void* v, const void* 
 
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                       bool in_bf16, bool out_bf16, hipStream_t s, bool gate_logits) {
+                       bool in_bf16, bool out_bf16, hipStream_t s, bool gate_logits,
+                       const void* z) {
   const bool L = gate_logits;
   if (in_bf16) {
-    return out_bf16 ? dispatch_decode_d<__bf16, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s, L)
-                    : dispatch_decode_d<__bf16, float>(q, k, v, g, beta, state, o, nh, dk, dv, s, L);
+    return out_bf16 ? dispatch_decode_d<__bf16, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s, L, z)
+                    : dispatch_decode_d<__bf16, float>(q, k, v, g, beta, state, o, nh, dk, dv, s, L, z);
   }
-  return out_bf16 ? dispatch_decode_d<float, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s, L)
-                  : dispatch_decode_d<float, float>(q, k, v, g, beta, state, o, nh, dk, dv, s, L);
+  return out_bf16 ? dispatch_decode_d<float, __bf16>(q, k, v, g, beta, state, o, nh, dk, dv, s, L, z)
+                  : dispatch_decode_d<float, float>(q, k, v, g, beta, state, o, nh, dk, dv, s, L, z);
 }
 
 }  // namespace kda

@@ -38,6 +38,12 @@ __device__ __forceinline__ float gamma_from_logit(float a) {
 // 2^x on the hardware transcendental unit.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Logistic sigmoid 1 / (1 + e^-z) of the output gate, from 2^x and a reciprocal on the
+// transcendental unit: z -> +inf gives 1, z -> -inf gives 0 (1 / inf), NaN stays NaN.
+__device__ __forceinline__ float sigmoid_hw(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
 // Two adjacent elements in one register: a bfloat16 pair (low half = lower
 // address) or a float32 pair.  pack2 rounds to nearest even.
 __device__ __forceinline__ uint32_t pack2(f32x2 x, uint32_t*) {

@@ -40,6 +40,8 @@ struct PrefillArgs {
   int64_t n_ck;
   // g holds raw decay logits a (log-decay = -softplus(a)) instead of log-decays
   int gate_logits;
+  // output gate z [B, T, H, dv] (input dtype) or NULL: o = (S^T q) * sigmoid(z)
+  const void* ogate;
 };
 
 // d_v slice width per prefill workgroup.
@@ -66,8 +68,10 @@ hipError_t multi_token(const void* q, const void* k, const void* v, const void* 
                        int64_t K, int64_t H, int dk, int dv, bool in_bf16, bool out_bf16,
                        bool commit, hipStream_t s);
 
+// ogate: output gate z [nh, dv] (input dtype) or NULL; o = (S^T q) * sigmoid(z)
 hipError_t decode_step(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, float* state, void* o, int64_t nh, int dk, int dv,
-                       bool in_bf16, bool out_bf16, hipStream_t s, bool gate_logits = false);
+                       bool in_bf16, bool out_bf16, hipStream_t s, bool gate_logits = false,
+                       const void* ogate = nullptr);
 
 }  // namespace kda

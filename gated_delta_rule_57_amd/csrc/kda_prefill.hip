@@ -149,7 +149,7 @@ struct PrefillLayout {
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-template <typename TIn, typename TOut, int DK, int DV, int DVS>
+template <typename TIn, typename TOut, int DK, int DV, int DVS, bool GATE>
 __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   typedef PrefillLayout<TIn, DK, DVS> Lay;
   constexpr bool BF16 = Lay::BF16;
@@ -295,6 +295,14 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 #pragma unroll
   for (int i = 0; i < NPV; ++i) pv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   TIn pbeta = from_f32<TIn>(0.f);  // kept raw: converting here would wait for the load
+  // output gate of the current chunk: one unit of 8 consecutive values of a row of the
+  // slice per thread (units 0 .. 64 DVS / 8 - 1), raw, loaded at the top of the chunk
+  constexpr int GU = DVS / 8;                 // gate units per row
+  constexpr int GPC = 8 * sizeof(TIn) / 16;   // 16-byte pieces per unit
+  static_assert(kC * GU <= NT, "one gate unit per thread");
+  float4 pz[GPC];
+#pragma unroll
+  for (int i = 0; i < GPC; ++i) pz[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   // token strides (elements); offsets inside one chunk fit in 32 bits
   const uint32_t rs_k = (uint32_t)(H * DK), rs_v = (uint32_t)(H * DV), rs_b = (uint32_t)H;
   // Rows past the end of the sequence load the last valid token (always in
@@ -399,6 +407,17 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     // are unconditional.
     const int64_t tn = (n + 1 < nchunks) ? t0 + kC : t0;
     prefetch(tn, 0);
+    if constexpr (GATE) {
+      if (emit && tid < kC * GU) {
+        const int r = min(tid / GU, (int)((te - t0) < kC ? (te - t0) : kC) - 1);
+        const int c = (tid % GU) * 8;
+        const TIn* zb = reinterpret_cast<const TIn*>(p.ogate) + ((b * T + t0) * H + h) * DV + j0;
+#pragma unroll
+        for (int i = 0; i < GPC; ++i)
+          pz[i] = ld_at<float4>(zb, ((uint32_t)r * rs_v + (uint32_t)c) * (uint32_t)sizeof(TIn) +
+                                        16u * (uint32_t)i);
+      }
+    }
     // ---- decay products: one thread per (channel pair, token range); the ranges'
     // products go to shared memory for the sub-tile offsets
     const int cp = tid % NCP, hr = tid / NCP, c0 = 2 * cp, r0 = RL * hr;
@@ -637,9 +656,12 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     constexpr int NKT = kC / KS;  // k-steps over the chunk's tokens
     const int kend = 16 * rt + 16;  // P rows of this tile vanish beyond kend
     f32x4 Oacc[NJW];
-    TOut* sO = reinterpret_cast<TOut*>(smem + Lay::O_A);  // [64][LDO] output staging
-    constexpr int LDO = DVS + 16 / (int)sizeof(TOut);
-    static_assert(kC * (DVS + 16 / (int)sizeof(TOut)) * (int)sizeof(TOut) <= Lay::SZ_AW, "O staging");
+    // output staging [64][LDO]: in the output dtype, or in float32 when the gate is
+    // applied at the store (one rounding, after the gate)
+    typedef typename std::conditional<GATE, float, TOut>::type stage_t;
+    stage_t* sO = reinterpret_cast<stage_t*>(smem + Lay::O_A);
+    constexpr int LDO = DVS + 16 / (int)sizeof(stage_t);
+    static_assert(kC * LDO * (int)sizeof(stage_t) <= Lay::SZ_AW, "O staging");
     {
       f32x4 y[NJW];
 #pragma unroll
@@ -780,7 +802,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         // O tile -> shared memory (A/W slot, free after the row-tile phase)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          sO[(16 * rt + 4 * lg + m) * LDO + 16 * jt + l16] = from_f32<TOut>(acc[m]);
+          sO[(16 * rt + 4 * lg + m) * LDO + 16 * jt + l16] = from_f32<stage_t>(acc[m]);
       }
     }
     {
@@ -809,7 +831,39 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
     }
     store_state_operand();  // only the row-tile phase reads it, and that phase is over
     __syncthreads();
-    if (emit) {  // output: one 16-byte store per piece, rows of DVS contiguous values
+    if (GATE && emit) {
+      // gated output: o * sigmoid(z) for this thread's unit of 8 values, rounded once
+      const int64_t ob = ((b * T + t0) * H + h) * DV + j0;
+      const int nvalid = (int)((te - t0) < kC ? (te - t0) : kC);
+      const int r = tid / GU, c = (tid % GU) * 8;
+      if (tid < kC * GU && r < nvalid) {
+        float z[8], y[8];
+        if constexpr (sizeof(TIn) == 2) {
+          unpack16(pz[0], (TIn*)nullptr, z);
+        } else {
+          unpack16(pz[0], (TIn*)nullptr, z);
+          unpack16(pz[GPC - 1], (TIn*)nullptr, z + 4);
+        }
+        const float* so = reinterpret_cast<const float*>(sO) + r * LDO + c;
+        const f32x4 y0 = *reinterpret_cast<const f32x4*>(so);
+        const f32x4 y1 = *reinterpret_cast<const f32x4*>(so + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = y0[e] * sigmoid_hw(z[e]);
+          y[4 + e] = y1[e] * sigmoid_hw(z[4 + e]);
+        }
+        const uint32_t off = ((uint32_t)r * rs_v + (uint32_t)c) * (uint32_t)sizeof(TOut);
+        if constexpr (sizeof(TOut) == 2) {
+          bf16x8 w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = (__bf16)y[e];
+          st_at<bf16x8>(go + ob, off, w);
+        } else {
+          st_at<f32x4>(go + ob, off, f32x4{y[0], y[1], y[2], y[3]});
+          st_at<f32x4>(go + ob, off + 16u, f32x4{y[4], y[5], y[6], y[7]});
+        }
+      }
+    } else if (emit) {  // output: one 16-byte store per piece, rows of DVS contiguous values
       constexpr int PPR = DVS * (int)sizeof(TOut) / 16;  // 16-byte pieces per row
       const int64_t ob = ((b * T + t0) * H + h) * DV + j0;
       const int nvalid = (int)((te - t0) < kC ? (te - t0) : kC);
@@ -878,7 +932,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
 template <typename TIn, typename TOut, int DK, int DV, int DVS>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   typedef PrefillLayout<TIn, DK, DVS> Lay;
-  auto kern = chunk_fwd_kernel<TIn, TOut, DK, DV, DVS>;
+  auto kern = a.ogate ? chunk_fwd_kernel<TIn, TOut, DK, DV, DVS, true>
+                      : chunk_fwd_kernel<TIn, TOut, DK, DV, DVS, false>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      Lay::TOTAL);
   if (e != hipSuccess) return e;

@@ -197,6 +197,33 @@ kda_status_t kda_recurrent_step_gate_logits(const void* q, const void* k, const 
                                             kda_dtype_t out, void* stream);
 
 /*
+ * Fused output gate.  These variants take one more input, the gate projection
+ *   gate  [B, T, H, dv] (prefill) or [N, H, dv] (decode), dtype `in`,
+ * and write o_t = (S_t^T q_t) * sigmoid(gate_t) elementwise, sigmoid(z) = 1 / (1 + e^-z),
+ * instead of S_t^T q_t: a full-scale (one value per token, head and value channel),
+ * input-dependent gate that decides which channels of the mixer's output a token
+ * reads.  The Towards-AI article on the Kimi K3 report describes such a gate on K3's
+ * Gated MLA layers and says it mirrors a similar gate in KDA (section "Gated MLA and No
+ * Position Encoding (NoPE)"); the logistic form is the plain reading where the page
+ * names no function.  The gate is applied before the output is rounded to `out` (one
+ * rounding).  States, checkpoints and everything else are as in kda_chunk_fwd /
+ * kda_recurrent_step; `gate` must be 16-byte aligned, non-NULL (KDA_ERR_NULL) and must
+ * not overlap o, the states or the workspace (KDA_ERR_ALIAS).  The projection that
+ * produces `gate` (weights) stays with the caller.
+ */
+kda_status_t kda_chunk_fwd_output_gate(const void* q, const void* k, const void* v, const void* g,
+                                       const void* beta, const void* gate,
+                                       const float* initial_state, void* o, float* final_state,
+                                       float* checkpoints, int64_t checkpoint_every, int64_t B,
+                                       int64_t T, int64_t H, int dk, int dv, int chunk,
+                                       kda_dtype_t in, kda_dtype_t out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+kda_status_t kda_recurrent_step_output_gate(const void* q, const void* k, const void* v,
+                                            const void* g, const void* beta, const void* gate,
+                                            float* state, void* o, int64_t N, int64_t H, int dk,
+                                            int dv, kda_dtype_t in, kda_dtype_t out, void* stream);
+
+/*
  * kda_chunk_fwd_checkpoints_at - kda_chunk_fwd with states saved at listed positions.
  *
  * Same as kda_chunk_fwd (same workspace) with checkpoint_every = 0, except that

@@ -30,6 +30,9 @@ from ``SeedSequence([seed, STATE_STREAM])``.
 
 Decode workloads draw the inputs of step ``s`` from ``SeedSequence([seed,
 DECODE_STREAM, s])``.
+
+Output-gate inputs (the gate projection z, one value per token, head and value
+channel) are z ~ N(0, 1), from ``SeedSequence([seed, GATE_STREAM])``.
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ import numpy as np
 BLOCK_T = 65536
 STATE_STREAM = 0x7FFF_0001
 DECODE_STREAM = 0x7FFF_0002
+GATE_STREAM = 0x7FFF_0003
 
 _SQRT2 = math.sqrt(2.0)
 
@@ -171,6 +175,15 @@ def prefill_inputs(w: Workload, t_end: Optional[int] = None, with_logits: bool =
            for i, n in enumerate(names)}
     out["s0"] = initial_state(w)
     return out
+
+
+def gate_inputs(w: Workload, shape=None) -> np.ndarray:
+    """Output-gate projection z ~ N(0, 1) with the shape of o ([B, T, H, dv] for a
+    prefill workload, or `shape`), rounded to the storage dtype; float64."""
+    if shape is None:
+        shape = (w.B, w.T, w.H, w.dv)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, GATE_STREAM])))
+    return round_to(rng.standard_normal(shape), w.dtype)
 
 
 def decode_step_inputs(w: Workload, step: int, seqs: Optional[slice] = None):

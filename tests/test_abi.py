@@ -246,3 +246,30 @@ def test_binding_checks_every_tensor_before_launch():
         kda.kda_recurrent_verify(q, k, v, g, beta, t(B, H, d, d, dtype=torch.float32)[:, :1])
     with pytest.raises((ValueError, TypeError)):
         kda.kda_chunk_fwd_checkpoints_at(q, k, v, g, beta, torch.zeros(2, dtype=torch.int32))
+
+
+def test_output_gate_entry_points_reject_before_launch(lib):
+    bf = kda.KDA_BF16
+    o = 64 * FAKE
+
+    def fwd(gate, o=o, **kw):
+        a = dict(B=1, T=64, H=1, dk=128, dv=128)
+        a.update(kw)
+        return lib.kda_chunk_fwd_output_gate(FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, gate,
+                                             None, o, None, None, 0, a["B"], a["T"], a["H"],
+                                             a["dk"], a["dv"], 64, bf, bf, None, 0, None)
+
+    assert fwd(None) == -1
+    assert fwd(7 * FAKE + 8) == -4
+    assert fwd(o + 64) == -6          # gate inside o
+    assert fwd(7 * FAKE, o=7 * FAKE + 256) == -6
+    assert fwd(7 * FAKE, dk=96) == -2
+
+    def step(gate, o=o):
+        return lib.kda_recurrent_step_output_gate(FAKE, 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE,
+                                                  gate, 6 * FAKE, o, 1, 1, 128, 128, bf, bf, None)
+
+    assert step(None) == -1
+    assert step(7 * FAKE + 4) == -4
+    assert step(o) == -6
+    assert step(6 * FAKE + 16) == -6  # gate inside the state
