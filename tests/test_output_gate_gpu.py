@@ -69,7 +69,8 @@ def test_prefill_gate_through_the_segment_path():
 
 @pytest.mark.parametrize("out_dtype", [None, torch.float32])
 def test_prefill_gate_closed_forms_bitwise(out_dtype):
-    """z = 0 halves o exactly; z = +60 passes it through, z = -60 closes it (bfloat16 z)."""
+    """z = 0 halves o exactly; z = +60 and +inf pass it through, z = -inf closes it; z = -60
+    scales it by sigmoid(-60) = 8.8e-27 (bfloat16 z)."""
     w = synth.PREFILL_B4_T4096.replace(B=1, T=150, H=2)
     x = synth.prefill_inputs(w)
     d = synth.to_torch(x, w.dtype, DEV)
@@ -80,10 +81,15 @@ def test_prefill_gate_closed_forms_bitwise(out_dtype):
     oh, _, _ = kda.kda_chunk_fwd(*args, out_dtype=out_dtype, output_gate=zeros)
     op, _, _ = kda.kda_chunk_fwd(*args, out_dtype=out_dtype, output_gate=zeros + 60.0)
     om, _, _ = kda.kda_chunk_fwd(*args, out_dtype=out_dtype, output_gate=zeros - 60.0)
+    opi, _, _ = kda.kda_chunk_fwd(*args, out_dtype=out_dtype, output_gate=zeros + float("inf"))
+    omi, _, _ = kda.kda_chunk_fwd(*args, out_dtype=out_dtype, output_gate=zeros - float("inf"))
     torch.cuda.synchronize()
-    assert torch.equal(op, o0)
+    assert torch.equal(op, o0) and torch.equal(opi, o0)
     assert torch.equal(oh, o0 * 0.5)
-    assert bool((om == 0).all())
+    assert bool((omi == 0).all())
+    sig = 1.0 / (1.0 + np.exp(60.0))
+    ratio = (om.double() / (o0.double() * sig))[o0 != 0]
+    assert float((ratio - 1).abs().max()) < 1e-2  # one rounding of o in the output dtype
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [("f32", 64, 64), ("bf16", 128, 128), ("bf16", 64, 128),
