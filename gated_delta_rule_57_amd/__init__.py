@@ -24,7 +24,7 @@ EXPORTS = ("kda_status_str", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
            "kda_chunk_fwd_segment_tokens", "kda_chunk_fwd_checkpoints_at", "kda_recurrent_step",
            "kda_recurrent_verify", "kda_recurrent_commit", "kda_chunk_fwd_gate_logits",
            "kda_recurrent_step_gate_logits", "kda_chunk_fwd_output_gate",
-           "kda_recurrent_step_output_gate")
+           "kda_recurrent_step_output_gate", "kda_chunk_fwd_noalloc")
 
 _lib = None
 
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_output_gate.argtypes = [vp] * 6 + list(lib.kda_chunk_fwd.argtypes[5:])
     lib.kda_recurrent_step_output_gate.restype = c_int
     lib.kda_recurrent_step_output_gate.argtypes = [vp] * 6 + list(lib.kda_recurrent_step.argtypes[5:])
+    lib.kda_chunk_fwd_noalloc.restype = c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = list(lib.kda_chunk_fwd.argtypes[:18]) + [vp]
     lib.kda_recurrent_verify.restype = c_int
     lib.kda_recurrent_verify.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, c_int, c_int,
                                          c_int, c_int, vp]
@@ -352,4 +354,31 @@ def kda_chunk_fwd_checkpoints_at(q, k, v, g, beta, positions, initial_state=None
         _dtype_code(q.dtype), _dtype_code(o.dtype), _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise KdaError(st, "kda_chunk_fwd_checkpoints_at")
+    return o, final_state, checkpoints
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, initial_state, o, final_state=None, *,
+                          checkpoint_every: int = 0, checkpoints=None, chunk: int = 64,
+                          stream=None):
+    """kda_chunk_fwd_noalloc: the chunked forward with the library's own device scratch as
+    the segment path's workspace.  Every output buffer is the caller's (nothing is
+    allocated here or in the library).  Returns (o, final_state, checkpoints)."""
+    B, T, H, dk, dv = _token_inputs(q, k, v, g, beta)
+    dev = q.device
+    _expect(o, "o", (B, T, H, dv), o.dtype if isinstance(o, torch.Tensor) else None, dev)
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", (B, H, dk, dv), torch.float32, dev)
+    if final_state is not None:
+        _expect(final_state, "final_state", (B, H, dk, dv), torch.float32, dev)
+    if checkpoints is not None or checkpoint_every:
+        if not checkpoint_every or checkpoints is None:
+            raise ValueError("checkpoints and checkpoint_every go together")
+        _expect(checkpoints, "checkpoints", (B, T // checkpoint_every, H, dk, dv),
+                torch.float32, dev)
+    st = load_library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+        _ptr(final_state), _ptr(checkpoints), int(checkpoint_every), B, T, H, dk, dv, chunk,
+        _dtype_code(q.dtype), _dtype_code(o.dtype), _stream(stream))
+    if st != 0:
+        raise KdaError(st, "kda_chunk_fwd_noalloc")
     return o, final_state, checkpoints

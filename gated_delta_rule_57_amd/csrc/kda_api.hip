@@ -5,8 +5,17 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_internal.h"
+
+// Workspace of kda_chunk_fwd_noalloc: a file-scope device array, so that the call
+// allocates nothing.  Every GPU the library runs on holds its own copy (loaded with
+// the library's code object, kept until the process ends).  Host code never uses
+// the array's name as an address: it uses the device address that
+// hipGetSymbolAddress reports for the current device (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 
 namespace {
@@ -129,7 +138,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
                             kda_dtype_t in, kda_dtype_t out, int64_t seg_len, void* workspace,
                             size_t workspace_bytes, void* stream, const int64_t* ck_pos = nullptr,
                             int64_t n_ck = 0, bool gate_logits = false,
-                            const void* ogate = nullptr) {
+                            const void* ogate = nullptr, bool validate_only = false) {
   if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
   if ((checkpoint_every != 0 || n_ck != 0) && !checkpoints) return KDA_ERR_NULL;
   if (n_ck != 0 && !ck_pos) return KDA_ERR_NULL;
@@ -146,7 +155,10 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
     return KDA_ERR_SHAPE;
   size_t off_z = 0, off_p = 0;
   const size_t ws_need = segment_workspace(B, H, nseg, dk, dv, &off_z, &off_p);
-  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
+  // validate_only: every check but the workspace's, then KDA_ERR_WORKSPACE when one is
+  // needed (KDA_OK when none is); nothing is launched
+  const bool ws_missing = ws_need > 0 && (!workspace || workspace_bytes < ws_need);
+  if (ws_missing && !validate_only) return KDA_ERR_WORKSPACE;
 
   const void* ptrs[] = {q,           k,           v,         g,     beta, initial_state, o,
                         final_state, checkpoints, workspace, ogate};
@@ -186,7 +198,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
     if (initial_state && overlaps(sc, span(initial_state, state_bytes))) return KDA_ERR_ALIAS;
     if (final_state && overlaps(sc, span(final_state, state_bytes))) return KDA_ERR_ALIAS;
   }
-  if (ws_need > 0) {
+  if (ws_need > 0 && !ws_missing) {
     const Span sw = span(workspace, (int64_t)ws_need);
     for (const Span& s : inputs)
       if (overlaps(sw, s)) return KDA_ERR_ALIAS;
@@ -197,6 +209,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
       return KDA_ERR_ALIAS;
   }
 
+  if (validate_only) return ws_missing ? KDA_ERR_WORKSPACE : KDA_OK;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, o, final_state,
                      nck > 0 ? checkpoints : nullptr, B, T, H, checkpoint_every,
@@ -420,4 +433,60 @@ extern "C" kda_status_t kda_chunk_fwd_output_gate(
   return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
                         checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
                         workspace_bytes, stream, nullptr, 0, false, gate);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of the scratch array on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                              const void* g, const void* beta,
+                                              const float* initial_state, void* o,
+                                              float* final_state, float* checkpoints,
+                                              int64_t checkpoint_every, int64_t B, int64_t T,
+                                              int64_t H, int dk, int dv, int chunk,
+                                              kda_dtype_t in, kda_dtype_t out, void* stream) {
+  if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return KDA_ERR_SHAPE;
+  const int64_t seg = auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16);
+  const int64_t nseg = num_segments(T, seg);
+  if (!mul_ok(B * H, nseg) || !mul_ok(B * H * nseg, (int64_t)dk * (2 * dv + dk) * 4))
+    return KDA_ERR_SHAPE;
+  const size_t need = segment_workspace(B, H, nseg, dk, dv, nullptr, nullptr);
+  if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    // the other arguments are checked first, so that a bad call touches no GPU state
+    const kda_status_t st0 =
+        chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
+                       checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, nullptr, 0,
+                       stream, nullptr, 0, false, nullptr, /*validate_only=*/true);
+    if (st0 != KDA_ERR_WORKSPACE) return st0;
+    if (scratch_address(&ws) != hipSuccess) return KDA_ERR_HIP;
+  }
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
+                        checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, ws,
+                        ws ? (size_t)KDA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }

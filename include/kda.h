@@ -49,6 +49,10 @@
 extern "C" {
 #endif
 
+/* Size of the device scratch array that kda_chunk_fwd_noalloc uses as its
+ * workspace (64 MiB per GPU). */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
 typedef enum {
@@ -286,6 +290,32 @@ kda_status_t kda_recurrent_verify(const void* q, const void* k, const void* v, c
 kda_status_t kda_recurrent_commit(const void* k, const void* v, const void* g, const void* beta,
                                   const int32_t* accept, float* state, int64_t N, int64_t K,
                                   int64_t H, int dk, int dv, kda_dtype_t in, void* stream);
+
+/*
+ * kda_chunk_fwd_noalloc - kda_chunk_fwd for callers that cannot allocate.
+ *
+ * For callers that may not call hipMalloc or any allocating routine: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * computation, arguments, outputs and errors as kda_chunk_fwd, without the workspace
+ * arguments: when the sizes call for the segment path, its workspace is a device
+ * array inside the library, KDA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, loaded with
+ * the library and held until the process ends.  The call itself allocates nothing.
+ *   - Sizes whose workspace (kda_chunk_fwd_workspace_bytes) exceeds
+ *     KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before anything else is
+ *     done; use kda_chunk_fwd with a workspace of your own for those.
+ *   - The first call on a device that needs the array looks up its address on that
+ *     device (hipGetSymbolAddress; KDA_ERR_HIP if that fails); the address is kept
+ *     per device.  Call with the device of `stream` current.
+ *   - Every call on one GPU shares that GPU's array, and nothing in it needs to start
+ *     at zero (each call writes what it reads).  Calls that overlap in time on one GPU
+ *     (different streams, or threads) race on the array: serialise them.
+ */
+kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta, const float* initial_state, void* o,
+                                   float* final_state, float* checkpoints,
+                                   int64_t checkpoint_every, int64_t B, int64_t T, int64_t H,
+                                   int dk, int dv, int chunk, kda_dtype_t in, kda_dtype_t out,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

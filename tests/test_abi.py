@@ -273,3 +273,24 @@ def test_output_gate_entry_points_reject_before_launch(lib):
     assert step(7 * FAKE + 4) == -4
     assert step(o) == -6
     assert step(6 * FAKE + 16) == -6  # gate inside the state
+
+
+def test_noalloc_rejects_before_launch(lib):
+    bf = kda.KDA_BF16
+
+    def call(**kw):
+        a = dict(q=FAKE, o=64 * FAKE, B=1, T=64, H=1, dk=128, dv=128, chunk=64)
+        a.update(kw)
+        return lib.kda_chunk_fwd_noalloc(a["q"], 2 * FAKE, 3 * FAKE, 4 * FAKE, 5 * FAKE, None,
+                                         a["o"], None, None, 0, a["B"], a["T"], a["H"], a["dk"],
+                                         a["dv"], a["chunk"], bf, bf, None)
+
+    assert call(q=None) == -1
+    assert call(dk=96) == -2
+    assert call(chunk=48) == -2
+    assert call(o=2 * FAKE) == -6
+    # a size that takes the segment path: the other arguments are checked before the
+    # library's scratch is looked up (no GPU call is made on the way to these errors)
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 65536, 32, 128, 128, 64, bf) > 0
+    assert call(q=None, T=65536, H=32) == -1
+    assert call(o=64 * FAKE + 4, T=65536, H=32) == -4
