@@ -72,9 +72,14 @@ constexpr int64_t kCUs = 256;
 // 131,071 for d = 128 (float32 output), far beyond any model's head count.
 constexpr int64_t kMaxChunkSpanBytes = 0xffffffffLL;
 
+// Chunk lengths: 64 (the default), 32 and 16 (bfloat16 inputs only).
+bool chunk_ok(int chunk, kda_dtype_t in) {
+  return chunk == 64 || ((chunk == 32 || chunk == 16) && in == KDA_BF16);
+}
+
 bool sizes_ok(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk, kda_dtype_t in) {
   if (!dtype_ok(in) || B < 1 || T < 1 || H < 1 || !head_dim_ok(dk) || !head_dim_ok(dv) ||
-      chunk != kChunk)
+      !chunk_ok(chunk, in))
     return false;
   if (in == KDA_F32 && (dk != 64 || dv != 64)) return false;
   const int64_t dmax = dk > dv ? dk : dv;
@@ -118,6 +123,14 @@ int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, boo
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// One launch of the chunk kernel for this chunk length: 64 tokens by the fused
+// 64-token kernel, 32 and 16 by the pipelined one.
+hipError_t launch_chunks(const kda::PrefillArgs& a, int chunk, int dk, int dv, bool in_bf16,
+                         bool out_bf16, hipStream_t st) {
+  if (chunk == 64) return kda::chunk_fwd(a, dk, dv, in_bf16, out_bf16, st);
+  return kda::chunk_fwd_pipe(a, chunk, dk, dv, out_bf16, st);
+}
 
 // Workspace of the segmented path: entry states and end-from-zero states
 // [B, nseg, H, dk, dv], transitions [B, nseg, H, dk, dk], float32.
@@ -224,13 +237,13 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
     s1.mode = 1;
     s1.seg_z = seg_z;
     s1.seg_p = seg_p;
-    hipError_t e = kda::chunk_fwd(s1, dk, dv, bf16, out == KDA_BF16, st);
+    hipError_t e = launch_chunks(s1, chunk, dk, dv, bf16, out == KDA_BF16, st);
     if (e == hipSuccess)
       e = kda::segment_scan(seg_z, seg_p, seg_in, B, H, nseg, dk, dv, st);
     if (e != hipSuccess) return KDA_ERR_HIP;
     a.seg_in = seg_in;
   }
-  const hipError_t e = kda::chunk_fwd(a, dk, dv, bf16, out == KDA_BF16, st);
+  const hipError_t e = launch_chunks(a, chunk, dk, dv, bf16, out == KDA_BF16, st);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

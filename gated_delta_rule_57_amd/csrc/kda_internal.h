@@ -54,6 +54,11 @@ int64_t prefill_grid(int64_t units, int slices);
 hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool out_bf16,
                      hipStream_t s);
 
+// The pipelined kernel for 32- or 16-token chunks (bfloat16 inputs; slices of 64 value
+// columns); same arguments and modes as chunk_fwd.
+hipError_t chunk_fwd_pipe(const PrefillArgs& a, int chunk, int dk, int dv, bool out_bf16,
+                          hipStream_t s);
+
 // Entry states of the segments after the first: seg_in[b, 1, h] = seg_z[b, 0, h] (the
 // summary of segment 0 starts from the initial state), seg_in[b, j+1, h] =
 // seg_p[b, j, h] seg_in[b, j, h] + seg_z[b, j, h].  Slot 0 is not written.  float32.

@@ -83,7 +83,12 @@ def test_chunk_fwd_rejects_before_launch(lib):
     assert _fwd(lib, o=o, din=7) == -3
     assert _fwd(lib, o=o, dk=96) == -2
     assert _fwd(lib, o=o, dv=256) == -2
-    assert _fwd(lib, o=o, chunk=32) == -2
+    assert _fwd(lib, o=o, chunk=48) == -2
+    assert _fwd(lib, o=o, chunk=128) == -2
+    # 16- and 32-token chunks take bfloat16 inputs only
+    assert _fwd(lib, o=o, chunk=32, din=kda.KDA_F32, dk=64, dv=64) == -2
+    assert _fwd(lib, o=o, chunk=16, din=kda.KDA_F32, dk=64, dv=64) == -2
+    assert _fwd(lib, o=o, chunk=32, every=48, ck=96 * FAKE) == -2  # not a multiple of the chunk
     assert _fwd(lib, o=o, T=0) == -2
     assert _fwd(lib, o=o, din=kda.KDA_F32, dk=128) == -2
     assert _fwd(lib, o=o, ck=96 * FAKE, every=100) == -2
