@@ -33,6 +33,12 @@ DECODE_STREAM, s])``.
 
 Output-gate inputs (the gate projection z, one value per token, head and value
 channel) are z ~ N(0, 1), from ``SeedSequence([seed, GATE_STREAM])``.
+
+Large-key inputs (``scale_keys``): each (token, head) query and key vector is
+rescaled to a norm drawn log-uniformly from [1, max_norm], and beta is redrawn as
+u * 1.9 / |k|^2 with u ~ U(0, 1), which keeps beta |k|^2 < 2 (so the factor
+1 - beta |k|^2 of the delta update along k stays inside (-1, 1)).  Draws come from
+``SeedSequence([seed, KEY_SCALE_STREAM])``.
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ BLOCK_T = 65536
 STATE_STREAM = 0x7FFF_0001
 DECODE_STREAM = 0x7FFF_0002
 GATE_STREAM = 0x7FFF_0003
+KEY_SCALE_STREAM = 0x7FFF_0004
 
 _SQRT2 = math.sqrt(2.0)
 
@@ -174,6 +181,24 @@ def prefill_inputs(w: Workload, t_end: Optional[int] = None, with_logits: bool =
     out = {n: round_to(np.concatenate([p[i] for p in parts], axis=1), w.dtype)
            for i, n in enumerate(names)}
     out["s0"] = initial_state(w)
+    return out
+
+
+def scale_keys(x: dict, w: Workload, max_norm: float = 30.0) -> dict:
+    """A copy of prefill inputs ``x`` (from ``prefill_inputs(w)``) with q and k of
+    norms log-uniform in [1, max_norm] per (token, head) and beta = u 1.9 / |k|^2,
+    u ~ U(0, 1), all rounded to the storage dtype; float64 arrays."""
+    shape = x["beta"].shape
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, KEY_SCALE_STREAM])))
+    lo, hi = 0.0, math.log(max_norm)
+    nq = np.exp(rng.uniform(lo, hi, shape))[..., None]
+    nk = np.exp(rng.uniform(lo, hi, shape))[..., None]
+    u = rng.uniform(0.0, 1.0, shape)
+    out = dict(x)
+    out["q"] = round_to(x["q"] / np.linalg.norm(x["q"], axis=-1, keepdims=True) * nq, w.dtype)
+    k = round_to(x["k"] / np.linalg.norm(x["k"], axis=-1, keepdims=True) * nk, w.dtype)
+    out["k"] = k
+    out["beta"] = round_to(u * 1.9 / np.sum(k * k, axis=-1), w.dtype)
     return out
 
 

@@ -67,3 +67,23 @@ def test_device_generator_laws_on_cpu():
     g = d["g"].float()
     assert bool((g >= -5).all()) and bool((g < 0).all())
     assert float((g == -5).float().mean()) > 0.3
+
+
+def test_scale_keys_recipe():
+    """Large-key inputs: norms in [1, 30], beta |k|^2 < 2, storage-dtype values, seeded,
+    v, g and the initial state untouched."""
+    w = synth.PREFILL_B4_T4096.replace(B=1, T=200, H=3, dk=64, dv=64, init_state=True)
+    x = synth.prefill_inputs(w)
+    a = synth.scale_keys(x, w)
+    b = synth.scale_keys(x, w)
+    for n in ("q", "k", "beta"):
+        assert np.array_equal(a[n], b[n])
+        assert np.array_equal(synth.round_to(a[n], w.dtype), a[n])
+    for n in ("v", "g", "s0"):
+        assert a[n] is x[n]
+    for n in ("q", "k"):
+        norms = np.linalg.norm(a[n], axis=-1)
+        assert norms.min() > 0.97 and norms.max() < 30.5
+        assert (norms > 15).mean() > 0.15 and (norms < 3).mean() > 0.15
+    bk = a["beta"] * np.sum(a["k"] ** 2, axis=-1)
+    assert bk.max() < 2.0 and bk.min() >= 0.0 and bk.mean() > 0.5
