@@ -54,6 +54,7 @@ extern "C" const char* kda_status_str(kda_status_t s) {
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+    default: break;
   }
   return "KDA_ERR_UNKNOWN";
 }
@@ -84,7 +85,9 @@ bool sizes_ok(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk, kda_dt
   if (in == KDA_F32 && (dk != 64 || dv != 64)) return false;
   const int64_t dmax = dk > dv ? dk : dv;
   if (H > kMaxChunkSpanBytes / (kChunk * dmax * 4)) return false;
-  return mul_ok(B, T) && mul_ok(B * T, H) && mul_ok(B * T * H, 128);
+  // the byte spans of the token tensors (tokens x d x element size, at most 4 bytes)
+  // stay inside int64
+  return mul_ok(B, T) && mul_ok(B * T, H) && mul_ok(B * T * H, 4 * dmax);
 }
 
 int64_t num_segments(int64_t T, int64_t seg_len) { return seg_len >= T ? 1 : (T + seg_len - 1) / seg_len; }

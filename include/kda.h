@@ -32,9 +32,12 @@
  *   - Arguments are validated on the host before anything is launched; a
  *     non-OK status means nothing was enqueued.  KDA_ERR_HIP reports a failed
  *     launch (hipGetLastError after the enqueue).
- *   - Supported sizes: d_k, d_v in {64, 128}; chunk == 64; T >= 1.  float32
- *     inputs support d_k = d_v = 64 (the float32-parity configuration);
- *     bfloat16 inputs support all four (d_k, d_v) pairs.
+ *   - Supported sizes: d_k, d_v in {64, 128}; T >= 1; chunk 64, or 32 and 16
+ *     with bfloat16 inputs.  float32 inputs support d_k = d_v = 64 (the
+ *     float32-parity configuration); bfloat16 inputs support all four (d_k, d_v)
+ *     pairs.  The chunked kernels address a chunk's token rows by 32-bit byte
+ *     offsets, so H may be at most (2^32 - 1) / (256 max(d_k, d_v)) (131,071 at
+ *     d = 128); larger H is KDA_ERR_SHAPE.
  *   - Pointers must be 16-byte aligned.
  *   - Concurrent calls on different streams are safe (the library is
  *     stateless); calls that write the same buffers race.
@@ -53,7 +56,16 @@ extern "C" {
  * workspace (64 MiB per GPU). */
 #define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+/* The two enumerations carry range sentinels (never valid arguments, never returned):
+ * they make every int a value of the type, so that a bad value passed from C or
+ * through a foreign-function interface is reported (KDA_ERR_DTYPE; "KDA_ERR_UNKNOWN")
+ * instead of being an out-of-range enumeration value inside the C++ library. */
+typedef enum {
+  KDA_F32 = 0,
+  KDA_BF16 = 1,
+  KDA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  KDA_DTYPE_RANGE_MAX_ = 0x7fffffff
+} kda_dtype_t;
 
 typedef enum {
   KDA_OK = 0,
@@ -63,7 +75,9 @@ typedef enum {
   KDA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
   KDA_ERR_WORKSPACE = -5, /* workspace missing or too small */
   KDA_ERR_ALIAS = -6,     /* an output overlaps an input it may not overlap */
-  KDA_ERR_HIP = -7        /* the HIP runtime reported an error at launch */
+  KDA_ERR_HIP = -7,       /* the HIP runtime reported an error at launch */
+  KDA_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  KDA_STATUS_RANGE_MAX_ = 0x7fffffff
 } kda_status_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -97,6 +111,12 @@ size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk, in
  *   checkpoints   [B, T / checkpoint_every, H, dk, dv] float32, or NULL.
  *                 Entry j is the state after token checkpoint_every*(j+1).
  *   checkpoint_every  0 = off; else a positive multiple of `chunk`.
+ *   chunk         64, or (bfloat16 inputs) 32 or 16.  64 runs a fused kernel
+ *                 whose phases take turns over one chunk; 32 and 16 run a
+ *                 pipelined kernel in which producer waves build chunk n+1's
+ *                 state-independent operands while consumer waves advance the
+ *                 state through chunk n.  All three compute the same result to
+ *                 within rounding.
  *   workspace / workspace_bytes  at least kda_chunk_fwd_workspace_bytes(...)
  *                 bytes (may be NULL when that is 0), else KDA_ERR_WORKSPACE.
  *                 Must not overlap any other buffer.
@@ -302,7 +322,9 @@ kda_status_t kda_recurrent_commit(const void* k, const void* v, const void* g, c
  * the library and held until the process ends.  The call itself allocates nothing.
  *   - Sizes whose workspace (kda_chunk_fwd_workspace_bytes) exceeds
  *     KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_WORKSPACE before anything else is
- *     done; use kda_chunk_fwd with a workspace of your own for those.
+ *     done; use kda_chunk_fwd with a workspace of your own for those.  (The
+ *     segmentation the library picks keeps its workspace near 30 MiB at most for
+ *     B <= 4, H <= 128, T <= 2^30, d = 128, so this is a guard.)
  *   - The first call on a device that needs the array looks up its address on that
  *     device (hipGetSymbolAddress; KDA_ERR_HIP if that fails); the address is kept
  *     per device.  Call with the device of `stream` current.
