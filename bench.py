@@ -1,8 +1,9 @@
 """Throughput of the KDA hot path on one MI355X, printed as one JSON line.
 
-A step is one kda_chunk_fwd (chunked prefill) over the 4 x 4096-token, 32-head,
-d = 128 bfloat16 workload with a float32 initial state, inputs resident in HBM.
-The same run also times kda_recurrent_step on the 256-sequence decode workload
+A step is one kda_chunk_fwd (chunked prefill, 64-token chunks) over the 4 x 4096-token,
+32-head, d = 128 bfloat16 workload with a float32 initial state, inputs resident in HBM.
+The same run also times that workload in 32-token chunks (the pipelined kernel),
+kda_recurrent_step on the 256-sequence decode workload
 (1000 chained steps), speculative verify / commit, the two few-head long-sequence
 prefill workloads (65,536 tokens x 32 heads, 1,048,576 tokens x 16 heads), and the
 float64 CPU oracle on a bounded sample.
@@ -10,6 +11,7 @@ float64 CPU oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -50,18 +52,26 @@ def commit_bytes(N, K, H, dk, dv, in_bytes=2) -> float:
     return N * H * (2 * dk * dv * 4 + K * ((2 * dk + dv + 1) * in_bytes))
 
 
+_CSRC = os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc")
+# the sources each kernel is compiled from (its own file and the shared headers)
+_SHARED = ("kda_device.h", "kda_internal.h")
 KERNEL_SOURCES = {
-    "prefill": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_prefill.hip"),
-    "decode": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
-    "verify": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
-    "commit": os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc", "kda_decode.hip"),
+    "prefill": ("kda_prefill.hip",) + _SHARED,
+    "prefill_chunk32": ("kda_prefill_pipe.hip",) + _SHARED,
+    "decode": ("kda_decode.hip",) + _SHARED,
+    "verify": ("kda_decode.hip",) + _SHARED,
+    "commit": ("kda_decode.hip",) + _SHARED,
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 COPY_CALIBRATION_BYTES = 1 << 30
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(which: str) -> str:
+    """sha256 (first 16 hex digits) over the sources of one kernel, in order."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[which]:
+        h.update(open(os.path.join(_CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(which: str):
@@ -71,7 +81,7 @@ def measured_traffic(which: str):
         rec = json.load(open(TRAFFIC_FILE))[which]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[which]):
+    if rec.get("source_sha256_16") != source_hash(which):
         return None
     return rec.get("bytes_per_launch")
 
@@ -96,7 +106,7 @@ def copy_calibration(torch, reps: int = 3):
                                            "GBps": 2 * COPY_CALIBRATION_BYTES / ms / 1e6}}))
 
 
-def time_prefill(kda, torch, w, steps, warmup):
+def time_prefill(kda, torch, w, steps, warmup, chunk=64, cold=True):
     import synth
 
     d = synth.device_prefill_inputs(w, "cuda")
@@ -105,7 +115,7 @@ def time_prefill(kda, torch, w, steps, warmup):
 
     def step():
         kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], o=o,
-                          final_state=sf)
+                          final_state=sf, chunk=chunk)
 
     for _ in range(warmup):
         step()
@@ -118,6 +128,8 @@ def time_prefill(kda, torch, w, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     assert bool(torch.isfinite(o.float()).all()), "non-finite prefill output"
+    if not cold:
+        return ms, None, None
     # the same launch with the last-level cache (256 MB MALL) flushed before each one by a
     # 512 MiB write, each launch timed on its own
     # (control: the same single-launch timing without the flush)
@@ -303,6 +315,12 @@ def main():
 
     import gated_delta_rule_57_amd as kda
 
+    # Python's cyclic garbage collector is paused while kernels are timed: a full
+    # collection stalls the launching thread for tens of milliseconds (a 31 ms idle gap
+    # between two back-to-back launches of a 0.1 ms kernel in one kernel trace), which
+    # is host noise, not time spent in the library
+    gc.collect()
+    gc.disable()
     ms, ms_cold, ms_single = time_prefill(kda, torch, w, args.steps, args.warmup)
     toks = w.B * w.T
     flops = prefill_flops_per_token_head(w.dk, w.dv) * toks * w.H
@@ -336,6 +354,17 @@ def main():
                        "note": "each launch timed alone after a 512 MiB write that flushes the "
                                "256 MB MALL; unflushed: the same single-launch timing without it"},
     }
+    # the same workload in 32-token chunks (the pipelined kernel); not the headline
+    ms32, _, _ = time_prefill(kda, torch, w, args.steps, args.warmup, chunk=32, cold=False)
+    gbs32, tf32 = nbytes / (ms32 * 1e-3) / 1e9, flops / (ms32 * 1e-3) / 1e12
+    line["prefill_chunk_32"] = {
+        "workload": w.name, "chunk": 32, "ms_per_step": ms32, "tokens_per_s": toks / (ms32 * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": gbs32, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs32 / HBM_PEAK_GBS, "traffic": measured_traffic("prefill_chunk32"),
+                     "kernel": "chunk_pipe_kernel<bf16,128,128,2>",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"achieved": tf32, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tf32 / BF16_MFMA_PEAK_TFLOPS}}
     if not args.no_decode:
         wd = synth.DECODE_N256
         us = time_decode(kda, torch, wd, args.decode_steps, 10)
@@ -368,6 +397,7 @@ def main():
     if not args.no_long:
         line["long_prefill"] = [time_long_prefill(kda, torch, wl)
                                 for wl in (synth.DECAY_FLOOR_T65536, synth.MILLION_TOKEN)]
+    gc.enable()
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
