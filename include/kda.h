@@ -224,10 +224,10 @@ kda_status_t kda_recurrent_step_gate_logits(const void* q, const void* k, const 
  * Fused output gate.  These variants take one more input, the gate projection
  *   gate  [B, T, H, dv] (prefill) or [N, H, dv] (decode), dtype `in`,
  * and write o_t = (S_t^T q_t) * sigmoid(gate_t) elementwise, sigmoid(z) = 1 / (1 + e^-z),
- * instead of S_t^T q_t: a full-scale (one value per token, head and value channel),
- * input-dependent gate that decides which channels of the mixer's output a token
- * reads.  The Towards-AI article on the Kimi K3 report describes such a gate on K3's
- * Gated MLA layers and says it mirrors a similar gate in KDA (section "Gated MLA and No
+ * instead of S_t^T q_t: one gate value per token, head and value channel, projected
+ * from the token's input by the caller, so each token chooses which channels of the
+ * mixer's output pass.  The Towards-AI article on the Kimi K3 report gives K3's Gated
+ * MLA layers such a gate and says KDA has a counterpart (section "Gated MLA and No
  * Position Encoding (NoPE)"); the logistic form is the plain reading where the page
  * names no function.  The gate is applied before the output is rounded to `out` (one
  * rounding).  States, checkpoints and everything else are as in kda_chunk_fwd /

@@ -213,10 +213,10 @@ def rel_l2_chunks(x, ref, chunk: int, t_axis: int = 1, group_axes=(0, 2)) -> np.
 def apply_output_gate(o, z):
     """KDA's output gate: o * sigmoid(z), elementwise, sigmoid(z) = 1 / (1 + e^-z).
 
-    z has o's shape (one gate value per token, head and value channel: a full-scale,
-    input-dependent gate that decides which channels of the output a token reads; the
-    Towards-AI article on the Kimi K3 report describes K3's Gated MLA gate this way and
-    says it mirrors a similar gate in KDA, section "Gated MLA and No Position Encoding
+    z has o's shape: one gate value per token, head and value channel, projected from
+    the token's input by the caller, so each token chooses which output channels pass.
+    The Towards-AI article on the Kimi K3 report gives K3's Gated MLA layers such a gate
+    and says KDA has a counterpart (section "Gated MLA and No Position Encoding
     (NoPE)").  The logistic form of the gate is the reading taken where the page names
     no function.  Float64; computed as e^z / (1 + e^z) for z < 0 so that neither
     branch overflows; NaN stays NaN."""

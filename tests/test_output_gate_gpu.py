@@ -1,7 +1,7 @@
 """Fused output gate: kda_chunk_fwd_output_gate and kda_recurrent_step_output_gate write
 o = (S^T q) * sigmoid(z), z one gate value per token, head and value channel (the gate the
-Towards-AI article on the Kimi K3 report describes for K3's Gated MLA and says mirrors one
-in KDA, section "Gated MLA and No Position Encoding (NoPE)").  Against the float64 oracle
+Towards-AI article on the Kimi K3 report gives K3's Gated MLA layers, with a counterpart in
+KDA, section "Gated MLA and No Position Encoding (NoPE)").  Against the float64 oracle
 (oracle.apply_output_gate on the oracle's o), and against the ungated call by closed forms
 that hold bit for bit: sigmoid(0) = 1/2, sigmoid(+large) = 1, sigmoid(-large) = 0."""
 import numpy as np
