@@ -15,6 +15,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
+# the range-check build of the same sources (include/kda_debug.h); for tests
+DEBUG_LIB_PATH = os.path.join(_PKG, "libkda_debug.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_NULL", -2: "KDA_ERR_SHAPE", -3: "KDA_ERR_DTYPE",

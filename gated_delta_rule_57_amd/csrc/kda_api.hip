@@ -9,6 +9,9 @@
 
 #include "kda.h"
 #include "kda_internal.h"
+#ifdef KDA_DEBUG_RANGE
+#include "kda_debug.h"
+#endif
 
 // Workspace of kda_chunk_fwd_noalloc: a file-scope device array, so that the call
 // allocates nothing.  Every GPU the library runs on holds its own copy (loaded with
@@ -127,6 +130,32 @@ int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, boo
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+#ifdef KDA_DEBUG_RANGE
+// Range-check build: the chunk kernels OR violation bits into this device word (one
+// copy per GPU), whose address is looked up once per device.
+static __device__ unsigned range_flags_word;
+constexpr int kMaxRangeDevices = 64;
+std::mutex g_range_mu;
+unsigned* g_range_ptr[kMaxRangeDevices];
+
+hipError_t range_flags_address(unsigned** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxRangeDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_range_mu);
+  if (!g_range_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(range_flags_word));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_range_ptr[dev] = static_cast<unsigned*>(p);
+  }
+  *out = g_range_ptr[dev];
+  return hipSuccess;
+}
+#endif
+
 // One launch of the chunk kernel for this chunk length: 64 tokens by the fused
 // 64-token kernel, 32 and 16 by the pipelined one.
 hipError_t launch_chunks(const kda::PrefillArgs& a, int chunk, int dk, int dv, bool in_bf16,
@@ -230,7 +259,10 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, o, final_state,
                      nck > 0 ? checkpoints : nullptr, B, T, H, checkpoint_every,
                      nseg > 1 ? seg_len : T, nseg, 0, nullptr, nullptr, nullptr,
-                     n_ck > 0 ? ck_pos : nullptr, n_ck, gate_logits ? 1 : 0, ogate};
+                     n_ck > 0 ? ck_pos : nullptr, n_ck, gate_logits ? 1 : 0, ogate, nullptr};
+#ifdef KDA_DEBUG_RANGE
+  if (range_flags_address(&a.range_flags) != hipSuccess) return KDA_ERR_HIP;
+#endif
   if (nseg > 1) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* seg_in = reinterpret_cast<float*>(ws);
@@ -506,3 +538,19 @@ extern "C" kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, cons
                         checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, ws,
                         ws ? (size_t)KDA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
+
+#ifdef KDA_DEBUG_RANGE
+extern "C" kda_status_t kda_debug_range_flags(unsigned* flags, int clear) {
+  if (!flags) return KDA_ERR_NULL;
+  unsigned* p = nullptr;
+  if (range_flags_address(&p) != hipSuccess) return KDA_ERR_HIP;
+  if (hipMemcpy(flags, p, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess)
+    return KDA_ERR_HIP;
+  if (clear) {
+    const unsigned zero = 0u;
+    if (hipMemcpy(p, &zero, sizeof(unsigned), hipMemcpyHostToDevice) != hipSuccess)
+      return KDA_ERR_HIP;
+  }
+  return KDA_OK;
+}
+#endif

@@ -35,6 +35,48 @@ __device__ __forceinline__ float gamma_from_logit(float a) {
   return (a != a) ? a : __builtin_amdgcn_fmed3f(t, kLogDecayFloor * kLog2e, 0.0f);
 }
 
+// ---- Range checks of the chunked forms (compiled in with -DKDA_DEBUG_RANGE only).
+// The -5 floor bounds a 16-token sub-tile's cumulative decay, so a diagonal tile's row
+// factor 2^L (L the inclusive log2-decay sum from the sub-tile's start) lies in
+// [e^-80, 1] and its column factor 2^-L in [1, e^80] (orkas.ai blog "Kimi K3
+// architecture", "A lower bound that deleted a GPU code path"), and every bfloat16
+// operand is then finite for moderate key norms.  A debug build checks the factors,
+// every operand, every kept A / P tile entry and the state after each chunk, and ORs
+// one bit per kind of violation into a device word; a release build compiles the
+// checks away.
+enum : unsigned {
+  kRangeFactor = 1u,   // a row factor outside [0, 1] or a column factor outside [1, e^80]
+  kRangeOperand = 2u,  // an operand not finite or beyond the bfloat16 range
+  kRangeTile = 4u,     // a kept entry of an A or P tile not finite
+  kRangeState = 8u,    // a state value not finite after a chunk
+};
+constexpr float kE80 = 5.5406224e34f;        // e^80
+constexpr float kBf16Max = 3.3895314e38f;    // largest finite bfloat16
+struct RangeCheck {
+  unsigned* flags;  // device word; NULL (or a release build): no checks
+#ifdef KDA_DEBUG_RANGE
+  __device__ __forceinline__ void operator()(bool bad, unsigned bit) const {
+    if (bad && flags) atomicOr(flags, bit);
+  }
+  // row factor 2^L in [0, 1], column factor 2^-L in [1, e^80] (one rounding of slack)
+  __device__ __forceinline__ void factors(float row, float col) const {
+    (*this)(!(row >= 0.f && row <= 1.f), kRangeFactor);
+    (*this)(!(col >= 0.99999f && col <= kE80 * 1.00001f), kRangeFactor);
+  }
+  __device__ __forceinline__ void operand(float x, float lim) const {
+    (*this)(!(__builtin_fabsf(x) <= lim), kRangeOperand);
+  }
+  __device__ __forceinline__ void finite(float x, unsigned bit) const {
+    (*this)(!(__builtin_fabsf(x) <= 3.4028235e38f), bit);
+  }
+#else
+  __device__ __forceinline__ void operator()(bool, unsigned) const {}
+  __device__ __forceinline__ void factors(float, float) const {}
+  __device__ __forceinline__ void operand(float, float) const {}
+  __device__ __forceinline__ void finite(float, unsigned) const {}
+#endif
+};
+
 // 2^x on the hardware transcendental unit.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -42,6 +42,8 @@ struct PrefillArgs {
   int gate_logits;
   // output gate z [B, T, H, dv] (input dtype) or NULL: o = (S^T q) * sigmoid(z)
   const void* ogate;
+  // range-check flag word (device) of a build with KDA_DEBUG_RANGE, else NULL
+  unsigned* range_flags;
 };
 
 // d_v slice width per prefill workgroup.

@@ -241,6 +241,7 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
   if (pmode && seg == 0) return;       // segment 0's transition is never used
   const int j0 = (pmode ? slice - NSLICE : slice) * DVS;
   const int64_t T = p.T, H = p.H;
+  const RangeCheck rc{p.range_flags};  // checks only in a KDA_DEBUG_RANGE build
   const int64_t tb = seg * p.seg_len;                             // first token
   const int64_t te = (T - tb) < p.seg_len ? T : tb + p.seg_len;   // one past the last
   // outputs (o, checkpoints, the final state) come from the output pass and, for
@@ -499,6 +500,13 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         const int r = r0 + j;
         const f32x2 kf = unpack2(ld2(sK + r * LDK + c0)), qf = unpack2(ld2(sQ + r * LDK + c0));
         const f32x2 kr = kf * ep[j], qr = qf * ep[j], kd = kf * em[j];
+        {
+          constexpr float lim = BF16 ? kBf16Max : 3.4028235e38f;
+          rc.factors(ep[j].x, em[j].x);
+          rc.factors(ep[j].y, em[j].y);
+          rc.operand(kr.x, lim), rc.operand(kr.y, lim), rc.operand(qr.x, lim);
+          rc.operand(qr.y, lim), rc.operand(kd.x, lim), rc.operand(kd.y, lim);
+        }
         st2(sK + r * LDK + c0, pack2(kr, (op2_t*)nullptr));
         const op2_t qh = pack2(qr, (op2_t*)nullptr);
         st2(sQ + r * LDK + c0, qh);
@@ -568,6 +576,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
         const int r = kSub * R + 4 * lg + m, i = col;
         sA[r * LDA + i] = (!DIAG || i < r) ? brow[m] * accA[m] : 0.f;
         sP[r * LDA + i] = (!DIAG || i <= r) ? accP[m] : 0.f;
+        rc.finite((!DIAG || i < r) ? accA[m] : 0.f, kRangeTile);
+        rc.finite((!DIAG || i <= r) ? accP[m] : 0.f, kRangeTile);
       }
       return DIAG ? accA * brow : accA;  // diagonal: beta-scaled A rows
     };
@@ -827,6 +837,8 @@ __global__ void __launch_bounds__(512) chunk_fwd_kernel(PrefillArgs p) {
           if constexpr (BF16) s = M::mma(ak, ul[q], s);
         }
         Sacc[i] = s;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) rc.finite(s[m], kRangeState);
       }
     }
     store_state_operand();  // only the row-tile phase reads it, and that phase is over

@@ -198,6 +198,7 @@ __global__ void __launch_bounds__(kPipeThreads) chunk_pipe_kernel(PrefillArgs p)
   if (pmode && seg == 0) return;
   const int j0 = (pmode ? slice - NSLICE : slice) * DVS;
   const int64_t T = p.T, H = p.H;
+  const RangeCheck rc{p.range_flags};  // checks only in a KDA_DEBUG_RANGE build
   const int64_t tb = seg * p.seg_len;
   const int64_t te = (T - tb) < p.seg_len ? T : tb + p.seg_len;
   const bool emit = p.mode == 0 || (seg == 0 && !pmode);
@@ -333,6 +334,10 @@ __global__ void __launch_bounds__(kPipeThreads) chunk_pipe_kernel(PrefillArgs p)
         const f32x2 ep = off * pre[j];
         const int r = tr0 + j;
         const f32x2 kr = kf * ep, qr = qf * ep, kd = kf * em;
+        rc.factors(ep.x, em.x);
+        rc.factors(ep.y, em.y);
+        rc.operand(kr.x, kBf16Max), rc.operand(kr.y, kBf16Max), rc.operand(qr.x, kBf16Max);
+        rc.operand(qr.y, kBf16Max), rc.operand(kd.x, kBf16Max), rc.operand(kd.y, kBf16Max);
         hkr[j] = kr;
         hqr[j] = qr;
         hkd[j] = kd;
@@ -429,6 +434,7 @@ __global__ void __launch_bounds__(kPipeThreads) chunk_pipe_kernel(PrefillArgs p)
       for (int m = 0; m < 4; ++m) {
         const int r = 4 * lg + m;
         N[m] = (c16 < r) ? brow[m] * na[m] : 0.f;
+        rc.finite(N[m], kRangeTile);
         Nt[m] = (r < c16) ? bcol * nt[m] : 0.f;
         I4[m] = (r == c16) ? 1.f : 0.f;
       }
@@ -452,8 +458,10 @@ __global__ void __launch_bounds__(kPipeThreads) chunk_pipe_kernel(PrefillArgs p)
       // P^T tiles (rows i = 4lg+m, column r = c16) -> P hi / lo rows r, paired token order
       auto put = [&](int R, int I, f32x4 pt, bool diag) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) {
           if (diag && 4 * lg + m > c16) pt[m] = 0.f;
+          rc.finite(pt[m], kRangeTile);
+        }
         const HL4 s = split4(pt);
         const int pos = 8 * lg + 4 * I;
         *reinterpret_cast<bf16x4*>(sPh + (16 * R + c16) * LDT + pos) = s.h;
@@ -655,6 +663,8 @@ __global__ void __launch_bounds__(kPipeThreads) chunk_pipe_kernel(PrefillArgs p)
       s = mma(kh, Ubl, s);
       s = mma(kl, Ubh, s);
       Sacc[ct] = s;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) rc.finite(s[m], kRangeState);
     }
   };
 

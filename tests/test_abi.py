@@ -299,3 +299,21 @@ def test_noalloc_rejects_before_launch(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(1, 65536, 32, 128, 128, 64, bf) > 0
     assert call(q=None, T=65536, H=32) == -1
     assert call(o=64 * FAKE + 4, T=65536, H=32) == -4
+
+
+def test_debug_library_exports_and_rejects_null():
+    """libkda_debug.so (the range-check build) exports every entry point of kda.h and the
+    flag reader of kda_debug.h, which rejects a NULL output before any GPU call."""
+    if not os.path.exists(kda.DEBUG_LIB_PATH):
+        pytest.skip("libkda_debug.so not built")
+    lib = kda.load_library(kda.DEBUG_LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    src = open(os.path.join(ROOT, "include", "kda_debug.h")).read()
+    for name in sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src))):
+        assert hasattr(lib, name), name
+    lib.kda_debug_range_flags.restype = ctypes.c_int
+    lib.kda_debug_range_flags.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert lib.kda_debug_range_flags(None, 0) == -1  # KDA_ERR_NULL
+    # the release library has no debug entry point
+    assert not hasattr(kda.load_library(), "kda_debug_range_flags")
