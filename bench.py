@@ -245,7 +245,9 @@ def time_long_prefill(kda, torch, w, reps: int = 3):
 
 
 def cpu_baseline(w, sample_batches: int):
-    """The float64 oracle on the first `sample_batches` sequences of the workload (all heads).
+    """The float64 oracle on `sample_batches` sequences of the workload's shape and laws (all
+    heads), host-drawn.  Returns the baseline record and the sample (inputs and the oracle's
+    outputs), which the GPU leg later runs through kda_chunk_fwd for the line's parity figures.
 
     Runs before this process touches the GPU: the oracle's worker pool is spawned here
     (started and warmed before the timed call, which then measures the oracle alone)."""
@@ -260,7 +262,7 @@ def cpu_baseline(w, sample_batches: int):
         oracle.kda_forward_heads_parallel(*[tiny[n] for n in ("q", "k", "v", "g", "beta")],
                                           x["s0"][:1], pool=pool)  # workers up and importing
         t = time.perf_counter()
-        _, procs = oracle.kda_forward_heads_parallel(*args, x["s0"], pool=pool)
+        (o_ref, s_ref, _), procs = oracle.kda_forward_heads_parallel(*args, x["s0"], pool=pool)
         dt = time.perf_counter() - t
     tokens = nb * w.T
     # one process on a smaller sample (two heads of one sequence), scaled to all heads
@@ -270,12 +272,47 @@ def cpu_baseline(w, sample_batches: int):
     oracle.kda_forward_heads_parallel(*[x1[n] for n in ("q", "k", "v", "g", "beta")],
                                       x["s0"][:1, :h1], processes=1)
     dt1 = time.perf_counter() - t
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": procs, "kind": "oracle",
-            "sample": f"{nb} of the {w.B} sequences x {w.T} tokens x {w.H} heads "
-                      f"({tokens * w.H} token-heads, {dt:.1f} s wall on {procs} processes)",
-            "single_core": {"value": w.T * h1 / w.H / dt1, "unit": "tokens/s",
-                            "sample": f"1 sequence x {w.T} tokens x {h1} heads on one process "
-                                      f"({dt1:.2f} s), scaled to {w.H} heads"}}
+    rec = {"value": tokens / dt, "unit": "tokens/s", "cores": procs, "kind": "oracle",
+           "sample": f"{nb} sequences x {w.T} tokens x {w.H} heads of the workload's shape and "
+                     f"laws, host-drawn ({tokens * w.H} token-heads, {dt:.1f} s wall on {procs} "
+                     "processes)",
+           "single_core": {"value": w.T * h1 / w.H / dt1, "unit": "tokens/s",
+                           "sample": f"1 sequence x {w.T} tokens x {h1} heads on one process "
+                                     f"({dt1:.2f} s), scaled to {w.H} heads"}}
+    return rec, {"x": x, "o": o_ref, "s": s_ref}
+
+
+def parity_of_sample(kda, torch, w, sample, tol=3e-3):
+    """The CPU leg's sample through kda_chunk_fwd (bf16 output, as timed) against the
+    oracle's outputs: relative L2 over each tensor, its maximum over (b, h), and for o its
+    maximum over 64-token windows of each head."""
+    import numpy as np
+    import synth
+
+    x = sample["x"]
+    d = synth.to_torch(x, w.dtype, "cuda")
+    o, s, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    torch.cuda.synchronize()
+    o = o.float().cpu().double().numpy()
+    s = s.cpu().double().numpy()
+
+    def rel(a, b, axes):
+        num = np.sqrt(np.sum((a - b) ** 2, axis=axes))
+        den = np.sqrt(np.sum(b ** 2, axis=axes))
+        return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+    o_ref, s_ref = sample["o"], sample["s"]
+    B, T, H, _ = o.shape
+    nw = T // 64
+    ow = rel(o[:, :nw * 64].reshape(B, nw, 64, H, -1), o_ref[:, :nw * 64].reshape(B, nw, 64, H, -1),
+             (2, 4))
+    out = {"sample": f"the CPU leg's {B} x {T} x {H} sample, bf16 output", "tol": tol,
+           "o_rel_l2": float(rel(o, o_ref, None)), "o_head_max": float(rel(o, o_ref, (1, 3)).max()),
+           "o_window_max": float(ow.max()), "state_rel_l2": float(rel(s, s_ref, None)),
+           "state_head_max": float(rel(s, s_ref, (2, 3)).max())}
+    out["pass"] = bool(max(out["o_rel_l2"], out["o_head_max"], out["state_rel_l2"],
+                           out["state_head_max"]) <= tol and out["o_window_max"] <= 2 * tol)
+    return out
 
 
 def main():
@@ -303,9 +340,9 @@ def main():
     w = synth.PREFILL_B4_T4096
     # the CPU leg first: its worker processes are started before anything here touches
     # the GPU
-    cpu = None
+    cpu = sample = None
     if not args.no_cpu_baseline and not args.copy_calibration:
-        cpu = cpu_baseline(w, args.cpu_sample_batches)
+        cpu, sample = cpu_baseline(w, args.cpu_sample_batches)
 
     import torch
 
@@ -400,6 +437,7 @@ def main():
     gc.enable()
     if cpu is not None:
         line["cpu_baseline"] = cpu
+        line["parity"] = parity_of_sample(kda, torch, w, sample)
     print(json.dumps(line), flush=True)
 
 
