@@ -2,7 +2,8 @@
 
 A step is one kda_chunk_fwd (chunked prefill, 64-token chunks) over the 4 x 4096-token,
 32-head, d = 128 bfloat16 workload with a float32 initial state, inputs resident in HBM.
-The same run also times that workload in 32-token chunks (the pipelined kernel),
+The same run also times that workload in 32-token chunks (the pipelined kernel) and
+through the output-gate, raw-logit and listed-checkpoint entry points,
 kda_recurrent_step on the 256-sequence decode workload
 (1000 chained steps), speculative verify / commit, the two few-head long-sequence
 prefill workloads (65,536 tokens x 32 heads, 1,048,576 tokens x 16 heads), and the
@@ -146,6 +147,53 @@ def time_prefill(kda, torch, w, steps, warmup, chunk=64, cold=True):
             out.append(e0.elapsed_time(e1))
     del scratch
     return ms, sum(cold) / len(cold), sum(single) / len(single)
+
+
+def time_variants(kda, torch, w, steps, warmup):
+    """The headline workload through the NEXT entry points, each timed like the headline
+    (warm-up, then `steps` back-to-back launches with HIP events on the current stream):
+    the fused output gate (one more [B,T,H,dv] input), raw decay logits (the same bytes,
+    -softplus in the gate step), and states saved at every 512th token (a prefix cache's
+    sparse block ends; 8 states per head written)."""
+    import synth
+
+    d = synth.device_prefill_inputs(w, "cuda")
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device="cuda")
+    sf = torch.empty_like(d["s0"])
+    z = torch.randn((w.B, w.T, w.H, w.dv), device="cuda").to(d["q"].dtype)
+    pos = torch.arange(512, w.T + 1, 512, dtype=torch.int64, device="cuda")
+    ck = torch.empty((w.B, pos.numel(), w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    base = prefill_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    legs = {
+        "output_gate": (lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                  d["s0"], o=o, final_state=sf, output_gate=z),
+                        base + w.B * w.T * w.H * w.dv * 2),
+        "gate_logits": (lambda: kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                  d["s0"], o=o, final_state=sf, gate_logits=True),
+                        base),
+        "checkpoints_every_512": (lambda: kda.kda_chunk_fwd_checkpoints_at(
+            d["q"], d["k"], d["v"], d["g"], d["beta"], pos, d["s0"], o=o, final_state=sf,
+            checkpoints=ck), base + ck.numel() * 4),
+    }
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, (fn, nbytes) in legs.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                  "algorithmic_bytes_per_launch": nbytes}}
+    assert bool(torch.isfinite(sf).all()), "non-finite state in the variant legs"
+    return out
 
 
 def time_decode(kda, torch, w, steps, warmup):
@@ -402,6 +450,7 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"achieved": tf32, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tf32 / BF16_MFMA_PEAK_TFLOPS}}
+    line["variants"] = time_variants(kda, torch, w, args.steps, args.warmup)
     if not args.no_decode:
         wd = synth.DECODE_N256
         us = time_decode(kda, torch, wd, args.decode_steps, 10)
