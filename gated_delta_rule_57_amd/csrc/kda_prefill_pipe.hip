@@ -42,7 +42,8 @@
 //       producers: gate, decay products and operands of chunk n+1 (one wave per
 //       sub-tile and quarter of the key channels); next chunk's loads issued
 //   I2  consumers: S <- 2^G_end S + Kbar^T U; checkpoints
-//       producers: Kc, Qc of chunk n+1; two waves invert I + A_RR, two build P
+//       producers: Kc, Qc of chunk n+1 (second sub-tile's waves); two waves invert
+//       I + A_RR, two build P
 //   I3  consumers: output stores
 //       producers: T' from the inverses, W and U0, Kbar and 2^G_end of chunk n+1
 // Every array the consumers read for chunk n is written for chunk n+1 in a later
@@ -377,29 +378,49 @@ __global__ void __launch_bounds__(kPipeThreads) chunk_pipe_kernel(PrefillArgs p)
   };
 
   // ---- I2 producer step, part 1: Kc^T (paired token order) and Qc (paired channel
-  // order) of the chunk whose operands were just built
+  // order) of the chunk whose operands were just built.  With two sub-tiles the second
+  // sub-tile's waves do both (the first sub-tile's waves are the ones that invert and
+  // build P in this interval).
   auto produce_kc_qc = [&]() {
     if (!act1) return;
-    f32x2 ref = {1.f, 1.f};  // 2^ref_R1: the product of the earlier sub-tile's decays
-    if (R1 == 1) ref = *reinterpret_cast<const f32x2*>(sTau + c0);
-    uint32_t kc[4];
+    if (NSUB == 2 && R1 == 0) return;
     const int pc = 32 * (c0 >> 5) + 8 * ((c0 & 15) >> 2) + 4 * ((c0 >> 4) & 1) + (c0 & 3);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = tr0 + j;
-      // k 2^G and q 2^G = (x 2^L) 2^ref
-      kc[j] = pack2(hkr[j] * ref, (uint32_t*)nullptr);
-      *reinterpret_cast<uint32_t*>(sQc + r * LDK + pc) = pack2(hqr[j] * ref, (uint32_t*)nullptr);
-    }
-    // per channel: tokens tr0..tr0+3 are one 4-group
-    {
-      const int pos = pt_pos(tr0);
+    // Kc^T rows c0, c0 + 1: four tokens from row t are one 4-group of the paired order
+    auto kct = [&](const uint32_t (&kc)[4], int t) {
+      const int pos = pt_pos(t);
       const uint32_t a0 = (kc[0] & 0xffffu) | (kc[1] << 16);
       const uint32_t a1 = (kc[2] & 0xffffu) | (kc[3] << 16);
       const uint32_t b0 = (kc[0] >> 16) | (kc[1] & 0xffff0000u);
       const uint32_t b1 = (kc[2] >> 16) | (kc[3] & 0xffff0000u);
       *reinterpret_cast<uint2*>(sKcT + c0 * LDT + pos) = make_uint2(a0, a1);
       *reinterpret_cast<uint2*>(sKcT + (c0 + 1) * LDT + pos) = make_uint2(b0, b1);
+    };
+    {
+      // this lane's own rows: k 2^G and q 2^G = (x 2^L) 2^ref, 2^ref the product of the
+      // earlier sub-tile's decays
+      f32x2 ref = {1.f, 1.f};
+      if (R1 == 1) ref = *reinterpret_cast<const f32x2*>(sTau + c0);
+      uint32_t kc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kc[j] = pack2(hkr[j] * ref, (uint32_t*)nullptr);
+        *reinterpret_cast<uint32_t*>(sQc + (tr0 + j) * LDK + pc) = pack2(hqr[j] * ref, (uint32_t*)nullptr);
+      }
+      kct(kc, tr0);
+    }
+    if constexpr (NSUB == 2) {
+      // the first sub-tile's rows 4 q1 .. +3, same channels: its reference is the chunk
+      // start, so Kc = k 2^L and Qc = q 2^L are the values already rounded into sKr and
+      // sQh, copied into the Kc^T and Qc layouts
+      const int t0 = 4 * q1;
+      uint32_t kc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kc[j] = *reinterpret_cast<const uint32_t*>(sKr + (t0 + j) * LDK + c0);
+        *reinterpret_cast<uint32_t*>(sQc + (t0 + j) * LDK + pc) =
+            *reinterpret_cast<const uint32_t*>(sQh + (t0 + j) * LDK + c0);
+      }
+      kct(kc, t0);
     }
   };
 
