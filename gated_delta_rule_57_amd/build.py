@@ -49,6 +49,21 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
 
 
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "kda_capi_main.c")
+CAPI_BIN = os.path.join(ROOT, "tests", "capi", "kda_capi_check")
+
+
+def build_capi_check(verbose: bool = True) -> str:
+    """The plain C caller used by the tests (tests/capi), linked against libkda.so."""
+    rocm = os.path.dirname(os.path.dirname(hipcc()))
+    _run(["gcc", "-O2", "-std=c11", "-Wall", "-I", os.path.join(ROOT, "include"),
+          "-I", os.path.join(rocm, "include"), "-D__HIP_PLATFORM_AMD__", CAPI_SRC,
+          "-L", PKG, "-lkda", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../../gated_delta_rule_57_amd",
+          "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", CAPI_BIN], verbose)
+    return CAPI_BIN
+
+
 def build(verbose: bool = True, debug_lib: bool = True) -> str:
     """Compile every source for each library variant (in parallel), link, and move the
     libraries into place.  Returns the path of libkda.so."""
@@ -65,6 +80,8 @@ def build(verbose: bool = True, debug_lib: bool = True) -> str:
             _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out + ".tmp"],
                  verbose)
             os.replace(out + ".tmp", out)
+    if os.path.exists(CAPI_SRC):
+        build_capi_check(verbose)
     return LIB
 
 
