@@ -13,6 +13,8 @@
 // 128-bit accesses; consecutive lanes cover consecutive 16-byte pieces of a
 // row, so a wavefront touches 1 KiB of contiguous state per access.  The two
 // column reductions (a and b) go through LDS once.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -125,19 +127,35 @@ __global__ void __launch_bounds__(256) decode_step_kernel(
 // architecture", section "The cost is paid in the serving stack", describes
 // this in place of rolling back an in-place update).
 //
-// One workgroup per (sequence, head) keeps the state slice in registers (as the
+// A workgroup keeps one (sequence, head) state slice in registers (as the
 // single-token kernel does) across the tokens.  The inputs of up to KB tokens are
 // loaded into shared memory at once (with the cumulative decays and k.q computed
 // there), so the token loop has no global loads and two barriers per token.
 // 512 threads (eight waves) keep RPT = 8 or fewer state rows x 4 columns per
-// thread: eight waves per SIMD fit for a commit, six for a verification (below).
-// 256-thread workgroups (twice the values per thread, fewer waves) measured 5-7%
-// slower; 1024 no faster for a commit and far slower for a verification.
+// thread.  256-thread workgroups (twice the values per thread, fewer waves)
+// measured 5-7% slower; 1024 no faster for a commit and far slower for a
+// verification.
+//
+// A verification only reads the state.  It loads it after the first block's own
+// inputs, so that staging the inputs and their decays need not wait for the 64 KiB
+// of state (loads retire in order), and with streaming loads, which keep it out of
+// the caches (-8% time together).  Asking for six waves per SIMD keeps it at 80
+// VGPRs, three workgroups per CU instead of two.  A commit writes its state back;
+// the same load order and streaming loads measured slower for it (and for the
+// single-token step), so it loads its state first, and fits eight waves per SIMD
+// without asking.
 constexpr int kMultiThreads = 512;
 
-// Verification holds more values per thread (the q sums and k.q); asking for six
-// waves per SIMD keeps it at 80 VGPRs, three workgroups per CU instead of two
-// (-15% time).  A commit already fits eight waves per SIMD and is left free.
+// A global-memory pointer that is the same in every lane, held in scalar
+// registers (so that a lane adds only a 32-bit offset to it).
+typedef const char __attribute__((address_space(1)))* global_cptr;
+__device__ __forceinline__ global_cptr uniform_ptr(const char* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (global_cptr)(((uint64_t)hi << 32) | lo);
+}
+
 template <typename TIn, typename TOut, int DK, int DV, bool COMMIT>
 __global__ void __launch_bounds__(kMultiThreads) __attribute__((amdgpu_waves_per_eu(COMMIT ? 1 : 6)))
 multi_token_kernel(
@@ -146,6 +164,8 @@ multi_token_kernel(
     float* __restrict__ state, TOut* __restrict__ o, int64_t N, int64_t K, int64_t H) {
   constexpr int NT = kMultiThreads, KB = 8;
   constexpr int CG = DV / 4, RG = NT / CG, RPT = DK / RG;
+  // element pairs of one block's [KB][DK] and [KB][DV] inputs per thread
+  constexpr int EP = (KB * DK / 2 + NT - 1) / NT, EQ = (KB * DV / 2 + NT - 1) / NT;
   static_assert(RPT * RG == DK && CG * RG == NT, "thread layout");
   constexpr bool WANT_O = !COMMIT;
   const int64_t hd = blockIdx.x;  // n * H + h
@@ -157,39 +177,105 @@ multi_token_kernel(
     steps = a < 0 ? 0 : (a > K ? K : a);
     if (steps == 0) return;
   }
-  const int t = threadIdx.x, cg = t % CG, rg = t / CG;
   // Inside a block the state is carried undecayed, S~ = Diag(Gamma_j)^-1 S with Gamma_j
   // the block's cumulative decay through token j: the decay moves from every state
   // element onto the token's key and query vectors (k Gamma_j, q Gamma_j, k / Gamma_j),
   // and the state is decayed once at the end of the block.  Gamma_j >= 2^(-5 log2e KB),
   // so 1 / Gamma_j stays a normal float.
   __shared__ float s_qg[WANT_O ? KB : 1][DK], s_kg[KB][DK], s_ki[KB][DK], s_v[KB][DV];
-  __shared__ float s_ge[DK], s_beta[KB], s_kq[KB];
+  // (for a verification, s_beta has a slot per thread: stored without a branch)
+  __shared__ float s_ge[DK], s_beta[WANT_O ? NT : KB], s_kq[KB];
   __shared__ float s_part_a[RG][DV], s_part_b[WANT_O ? RG : 1][DV];
   __shared__ float s_u[DV];
 
-  float4* st = reinterpret_cast<float4*>(state + hd * (int64_t)(DK * DV));
-  float4 S[RPT];
+  const int t = threadIdx.x, cg = t % CG, rg = t / CG;
+  auto load_state = [&](float4 (&X)[RPT], int64_t head) {
+    if constexpr (COMMIT) {
+      const float4* st = reinterpret_cast<const float4*>(state + head * (int64_t)(DK * DV));
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) S[i] = st[(rg + RG * i) * CG + cg];
+      for (int i = 0; i < RPT; ++i) X[i] = st[(rg + RG * i) * CG + cg];
+      return;
+    }
+    // a uniform 64-bit base and one 32-bit lane offset: rows step by a constant
+    const char* src = reinterpret_cast<const char*>(state + head * (int64_t)(DK * DV));
+    const uint32_t lane_off = (uint32_t)(rg * CG + cg) * 16u;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      typedef const f32x4 __attribute__((address_space(1)))* gf4;
+      const gf4 p = (gf4)(uniform_ptr(src + (size_t)i * (RG * CG * 16)) + lane_off);
+      const f32x4 x = __builtin_nontemporal_load(p);
+      X[i] = float4{x[0], x[1], x[2], x[3]};
+    }
+  };
+  float4 S[RPT];
+  if (COMMIT) load_state(S, hd);
 
-  for (int64_t j0 = 0; j0 < steps; j0 += KB) {
+  // One block of up to KB tokens; a verification's first block is its own copy, so
+  // that its state loads sit in straight-line code behind the inputs.
+  auto block = [&](int64_t j0, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
     const int nb = (int)((steps - j0) < KB ? (steps - j0) : KB);
-    if (j0 > 0) __syncthreads();  // the previous block is done with the inputs
-    // this block's inputs (token j of the draft is [n, j, h]), raw: k, g (in the slot of
-    // k / Gamma), q, v, beta
-    for (int e = t; e < nb * DK; e += NT) {
-      const int j = e / DK, c = e % DK;
-      const int64_t off = ((n * K + j0 + j) * H + h) * DK + c;
-      if (WANT_O) s_qg[j][c] = to_f32(q[off]);
-      s_kg[j][c] = to_f32(k[off]);
-      s_ki[j][c] = to_f32(g[off]);
+    if (!FIRST && j0 > 0) __syncthreads();  // the previous block is done with the inputs
+    // this block's inputs (token j of the draft is [n, j, h]), raw: k, g (in the slot
+    // of k / Gamma), q, v, beta
+    if constexpr (COMMIT) {
+      for (int e = t; e < nb * DK; e += NT) {
+        const int j = e / DK, c = e % DK;
+        const int64_t off = ((n * K + j0 + j) * H + h) * DK + c;
+        s_kg[j][c] = to_f32(k[off]);
+        s_ki[j][c] = to_f32(g[off]);
+      }
+      for (int e = t; e < nb * DV; e += NT) {
+        const int j = e / DV, c = e % DV;
+        s_v[j][c] = to_f32(v[((n * K + j0 + j) * H + h) * DV + c]);
+      }
+      if (t < nb) s_beta[t] = to_f32(beta[(n * K + j0 + t) * H + h]);
+    } else {
+      // Loaded into registers first, two consecutive elements per thread and load,
+      // so that the state loads queue behind them; a token past the block's end
+      // loads the block's last token (in bounds) into a row that is never read,
+      // which keeps loads and stores free of branches
+      typedef TIn pair_t __attribute__((ext_vector_type(2)));
+      float xk[EP][2], xg[EP][2], xq[EP][2], xv[EQ][2];
+#pragma unroll
+      for (int i = 0; i < EP; ++i) {
+        const int e = 2 * (t + NT * i);
+        const int j = min(e / DK, nb - 1), c = e % DK;  // (in bounds for any e)
+        const int64_t off = ((n * K + j0 + j) * H + h) * DK + c;
+        const pair_t a = *reinterpret_cast<const pair_t*>(&q[off]);
+        const pair_t b = *reinterpret_cast<const pair_t*>(&k[off]);
+        const pair_t d = *reinterpret_cast<const pair_t*>(&g[off]);
+        xq[i][0] = to_f32(a[0]), xq[i][1] = to_f32(a[1]);
+        xk[i][0] = to_f32(b[0]), xk[i][1] = to_f32(b[1]);
+        xg[i][0] = to_f32(d[0]), xg[i][1] = to_f32(d[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < EQ; ++i) {
+        const int e = 2 * (t + NT * i);
+        const int j = min(e / DV, nb - 1), c = e % DV;
+        const pair_t a = *reinterpret_cast<const pair_t*>(&v[((n * K + j0 + j) * H + h) * DV + c]);
+        xv[i][0] = to_f32(a[0]), xv[i][1] = to_f32(a[1]);
+      }
+      const float xb = to_f32(beta[(n * K + j0 + min(t, nb - 1)) * H + h]);
+      if (FIRST) load_state(S, hd);  // (a verification's; a commit's are issued above)
+#pragma unroll
+      for (int i = 0; i < EP; ++i) {
+        const int e = 2 * (t + NT * i);
+        if (KB * DK / 2 % NT == 0 || e < KB * DK) {
+          const int j = e / DK, c = e % DK;
+          s_qg[j][c] = xq[i][0], s_qg[j][c + 1] = xq[i][1];
+          s_kg[j][c] = xk[i][0], s_kg[j][c + 1] = xk[i][1];
+          s_ki[j][c] = xg[i][0], s_ki[j][c + 1] = xg[i][1];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < EQ; ++i) {
+        const int e = 2 * (t + NT * i);
+        if (KB * DV / 2 % NT == 0 || e < KB * DV)
+          s_v[e / DV][e % DV] = xv[i][0], s_v[e / DV][e % DV + 1] = xv[i][1];
+      }
+      s_beta[t] = xb;  // slots past the block's tokens are never read
     }
-    for (int e = t; e < nb * DV; e += NT) {
-      const int j = e / DV, c = e % DV;
-      s_v[j][c] = to_f32(v[((n * K + j0 + j) * H + h) * DV + c]);
-    }
-    if (t < nb) s_beta[t] = to_f32(beta[(n * K + j0 + t) * H + h]);
     __syncthreads();
     if (t < DK) {  // one thread per key channel: the cumulative decay over the block
       const int c = t;
@@ -271,12 +357,19 @@ multi_token_kernel(
         S[i].w *= ge;
       }
     }
+  };
+  if constexpr (COMMIT) {
+    for (int64_t j0 = 0; j0 < steps; j0 += KB) block(j0, std::false_type{});
+  } else {
+    block(int64_t(0), std::true_type{});
+    for (int64_t j0 = KB; j0 < steps; j0 += KB) block(j0, std::false_type{});
   }
   if (COMMIT) {
+    f32x4* dst = reinterpret_cast<f32x4*>(state + hd * (int64_t)(DK * DV));
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       __builtin_nontemporal_store(f32x4{S[i].x, S[i].y, S[i].z, S[i].w},
-                                  reinterpret_cast<f32x4*>(&st[(rg + RG * i) * CG + cg]));
+                                  &dst[(rg + RG * i) * CG + cg]);
   }
 }
 
@@ -312,11 +405,14 @@ template <typename TIn, typename TOut, bool COMMIT>
 hipError_t launch_multi(const void* q, const void* k, const void* v, const void* g,
                         const void* beta, const int32_t* accept, float* state, void* o, int64_t N,
                         int64_t K, int64_t H, int dk, int dv, hipStream_t s) {
-  const dim3 grid((unsigned)(N * H)), block(kMultiThreads);
+  const dim3 block(kMultiThreads);
 #define KDA_MULTI(DK_, DV_)                                                                     \
-  multi_token_kernel<TIn, TOut, DK_, DV_, COMMIT><<<grid, block, 0, s>>>(                       \
-      (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, accept, state, \
-      (TOut*)o, N, K, H)
+  do {                                                                                          \
+    auto* kern = multi_token_kernel<TIn, TOut, DK_, DV_, COMMIT>;                              \
+    kern<<<dim3((unsigned)(N * H)), block, 0, s>>>(                                             \
+        (const TIn*)q, (const TIn*)k, (const TIn*)v, (const TIn*)g, (const TIn*)beta, accept,   \
+        state, (TOut*)o, N, K, H);                                                              \
+  } while (0)
   if (dk == 128 && dv == 128) KDA_MULTI(128, 128);
   else if (dk == 64 && dv == 64) KDA_MULTI(64, 64);
   else if (dk == 64 && dv == 128) KDA_MULTI(64, 128);
