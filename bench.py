@@ -57,7 +57,7 @@ _CSRC = os.path.join(ROOT, "gated_delta_rule_57_amd", "csrc")
 # the sources each kernel is compiled from (its own file and the shared headers)
 _SHARED = ("kda_device.h", "kda_internal.h")
 KERNEL_SOURCES = {
-    "prefill": ("kda_prefill.hip",) + _SHARED,
+    "prefill": ("kda_prefill.hip", "kda_prefill_body.inc") + _SHARED,
     "prefill_chunk32": ("kda_prefill_pipe.hip",) + _SHARED,
     "decode": ("kda_decode.hip",) + _SHARED,
     "verify": ("kda_decode.hip",) + _SHARED,

@@ -103,6 +103,7 @@ int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, boo
   const int64_t nch = (T + kChunk - 1) / kChunk;
   const int sl = kda::prefill_slice(dk, dv, bf16);
   const int64_t ns = dv / sl, np = dk / sl;
+  const bool split = kda::summary_split_ok(dk, dv, bf16, (int)kChunk);
   auto rounds = [](int64_t wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
   const double one = rounds(B * H * ns) * (double)nch;
   double best = one;
@@ -114,7 +115,11 @@ int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, boo
     // summaries: zero-start states of segments 0 .. n-2 (segment 0 from the initial
     // state, writing its outputs too) and transitions of segments 1 .. n-2; outputs:
     // segments 1 .. n-1
-    const double summary = rounds(B * H * ((n - 1) * (ns + np) - np)) * (double)segc;
+    // (with the split summary pass, segments 1 .. n-2 take two 128-column workgroups
+    // each, whose chunk steps cost about as much as an ordinary one)
+    const int64_t wg_summary = (split && n >= 3) ? B * H * (ns + 2 * (n - 2))
+                                                 : B * H * ((n - 1) * (ns + np) - np);
+    const double summary = rounds(wg_summary) * (double)segc;
     const double outputs = rounds(B * (n - 1) * H * ns) * (double)segc;
     // a scan step costs about a third of a chunk step; the two extra launches
     // about a chunk step each
@@ -272,7 +277,18 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
     s1.mode = 1;
     s1.seg_z = seg_z;
     s1.seg_p = seg_p;
-    hipError_t e = launch_chunks(s1, chunk, dk, dv, bf16, out == KDA_BF16, st);
+    hipError_t e;
+    if (nseg >= 3 && kda::summary_split_ok(dk, dv, bf16, chunk)) {
+      // segment 0 by the ordinary workgroups; the zero-start states and transitions of
+      // segments 1 .. nseg-2 by the 128-column summary workgroups, in the same launch
+      kda::PrefillArgs a0 = s1, a1 = s1;
+      a0.seg_first = 0, a0.seg_count = 1, a0.with_p = 0;
+      a1.seg_first = 1, a1.seg_count = nseg - 2, a1.with_p = 1;
+      a1.ogate = nullptr;
+      e = kda::chunk_fwd_summary(a0, a1, out == KDA_BF16, st);
+    } else {
+      e = launch_chunks(s1, chunk, dk, dv, bf16, out == KDA_BF16, st);
+    }
     if (e == hipSuccess)
       e = kda::segment_scan(seg_z, seg_p, seg_in, B, H, nseg, dk, dv, st);
     if (e != hipSuccess) return KDA_ERR_HIP;

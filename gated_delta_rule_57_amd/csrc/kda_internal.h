@@ -44,6 +44,11 @@ struct PrefillArgs {
   const void* ogate;
   // range-check flag word (device) of a build with KDA_DEBUG_RANGE, else NULL
   unsigned* range_flags;
+  // When seg_count > 0 the launch covers segments seg_first .. seg_first + seg_count - 1
+  // only (instead of the ranges above), and a mode-1 launch has transition ("P")
+  // workgroups only if with_p.  Used by the split summary pass (chunk_fwd_summary).
+  int64_t seg_first = 0, seg_count = 0;
+  int with_p = 1;
 };
 
 // d_v slice width per prefill workgroup.
@@ -55,6 +60,18 @@ int64_t prefill_grid(int64_t units, int slices);
 
 hipError_t chunk_fwd(const PrefillArgs& a, int dk, int dv, bool in_bf16, bool out_bf16,
                      hipStream_t s);
+
+// Whether the split summary pass below serves these sizes (bfloat16 inputs, d_k = d_v =
+// 128, 64-token chunks).
+bool summary_split_ok(int dk, int dv, bool in_bf16, int chunk);
+
+// The summary pass (mode 1) of a segmented launch as one kernel of two parts: the
+// workgroups of segment 0 (a0: from the initial state, writing that segment's outputs,
+// no transition workgroups) and, for segments 1 .. nseg-2 (a1), one workgroup for the
+// zero-start state and one for the transition, each carrying all 128 columns and none
+// of the query or output work.
+hipError_t chunk_fwd_summary(const PrefillArgs& a0, const PrefillArgs& a1, bool out_bf16,
+                             hipStream_t s);
 
 // The pipelined kernel for 32- or 16-token chunks (bfloat16 inputs; slices of 64 value
 // columns); same arguments and modes as chunk_fwd.
