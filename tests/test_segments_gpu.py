@@ -157,3 +157,54 @@ def test_library_choice_of_segments_for_few_heads():
     print(f"[segments] library choice {seg}", flush=True)
     parity.check("o", o, o_r, 3e-3, "tokens")
     parity.check("final state", s, s_r, 3e-3, "state")
+
+
+@pytest.mark.parametrize("variant", ["plain", "checkpoints"])
+@pytest.mark.parametrize("nseg", [2, 3, 5])
+def test_split_summary_pass(nseg, variant):
+    """bfloat16, d = 128, 64-token chunks: from three segments on, the summary pass runs
+    segment 0 on the ordinary workgroups (its outputs and checkpoints included) and the
+    later segments' zero-start states and transitions on 128-column workgroups, in one
+    launch; two segments keep the ordinary summary launch.  Ragged last segment."""
+    seg = 192
+    w = synth.PREFILL_B4_T4096.replace(B=2, T=seg * (nseg - 1) + 70, H=2, seed=700 + nseg)
+    x = synth.prefill_inputs(w)
+    d = synth.to_torch(x, w.dtype, DEV)
+    print(f"[segments] split summary pass: {nseg} segments, {variant}", flush=True)
+    every = 128 if variant == "checkpoints" else 0  # boundaries inside segment 0 and later
+    o, s, ck = _run(d, seg, out_dtype=torch.float32, checkpoint_every=every)
+    torch.cuda.synchronize()
+    o_r, s_r, ck_r = _ref(x, every)
+    parity.check("o", o, o_r, TOL["bf16"], "tokens")
+    parity.check("final state", s, s_r, TOL["bf16"], "state")
+    if every:
+        parity.check("checkpoints", ck, ck_r, TOL["bf16"], "ckpt")
+
+
+@pytest.mark.parametrize("variant", ["output_gate", "gate_logits"])
+def test_split_summary_pass_library_segments(variant):
+    """The gated and raw-logit entries take the library's own segment length: 8 segments at
+    this size, so the split summary pass runs (the gate on segment 0's outputs there, the
+    logits in both kinds of workgroup)."""
+    w = synth.PREFILL_B4_T4096.replace(B=2, T=1000, H=2, seed=711)
+    seg = kda.kda_chunk_fwd_segment_tokens(w.B, w.T, w.H, w.dk, w.dv)
+    assert -(-w.T // seg) >= 3
+    x = synth.prefill_inputs(w, with_logits=variant == "gate_logits")
+    names = ["q", "k", "v", "g", "beta", "s0"] + (["a"] if variant == "gate_logits" else [])
+    d = synth.to_torch({n: x[n] for n in names}, w.dtype, DEV)
+    print(f"[segments] split summary pass, {variant}: {-(-w.T // seg)} segments", flush=True)
+    if variant == "output_gate":
+        z = synth.gate_inputs(w)
+        o, s, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"],
+                                    out_dtype=torch.float32,
+                                    output_gate=synth.to_torch({"z": z}, w.dtype, DEV)["z"])
+        o_r, s_r, _ = _ref(x)
+        o_r = oracle.apply_output_gate(o_r, z)
+    else:
+        o, s, _ = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["a"], d["beta"], d["s0"],
+                                    out_dtype=torch.float32, gate_logits=True)
+        (o_r, s_r, _), _ = oracle.kda_forward_heads_parallel(
+            x["q"], x["k"], x["v"], oracle.log_decay_from_logits(x["a"]), x["beta"], x["s0"], 0)
+    torch.cuda.synchronize()
+    parity.check("o", o, o_r, TOL["bf16"], "tokens")
+    parity.check("final state", s, s_r, TOL["bf16"], "state")
