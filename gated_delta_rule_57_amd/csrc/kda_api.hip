@@ -99,11 +99,12 @@ int64_t num_segments(int64_t T, int64_t seg_len) { return seg_len >= T ? 1 : (T 
 // model of the three launches (summaries, scan, outputs) when that beats one
 // segment by 20% or more; T rounded up to whole chunks (one segment) otherwise.
 // Deterministic in the sizes.
-int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, bool bf16) {
+int64_t auto_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv, bool bf16,
+                            int chunk) {
   const int64_t nch = (T + kChunk - 1) / kChunk;
   const int sl = kda::prefill_slice(dk, dv, bf16);
   const int64_t ns = dv / sl, np = dk / sl;
-  const bool split = kda::summary_split_ok(dk, dv, bf16, (int)kChunk);
+  const bool split = kda::summary_split_ok(dk, dv, bf16, chunk);
   auto rounds = [](int64_t wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
   const double one = rounds(B * H * ns) * (double)nch;
   double best = one;
@@ -303,7 +304,7 @@ kda_status_t chunk_fwd_impl(const void* q, const void* k, const void* v, const v
 extern "C" int64_t kda_chunk_fwd_segment_tokens(int64_t B, int64_t T, int64_t H, int dk, int dv,
                                                 int chunk, kda_dtype_t in) {
   if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return 0;
-  return auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16);
+  return auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk);
 }
 
 extern "C" size_t kda_chunk_fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int dk,
@@ -320,7 +321,7 @@ extern "C" size_t kda_chunk_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H,
                                                 int chunk, kda_dtype_t in) {
   if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return 0;
   return kda_chunk_fwd_segmented_workspace_bytes(
-      B, T, H, dk, dv, chunk, in, auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16));
+      B, T, H, dk, dv, chunk, in, auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk));
 }
 
 extern "C" kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
@@ -330,7 +331,7 @@ extern "C" kda_status_t kda_chunk_fwd(const void* q, const void* k, const void* 
                                       int dk, int dv, int chunk, kda_dtype_t in, kda_dtype_t out,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
-                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk)
                           : kChunk;
   return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
                         checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
@@ -465,7 +466,7 @@ extern "C" kda_status_t kda_chunk_fwd_checkpoints_at(
     void* stream) {
   if (n_positions < 1) return KDA_ERR_SHAPE;
   const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
-                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk)
                           : kChunk;
   return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints, 0, B, T, H,
                         dk, dv, chunk, in, out, seg, workspace, workspace_bytes, stream, positions,
@@ -478,7 +479,7 @@ extern "C" kda_status_t kda_chunk_fwd_gate_logits(
     int64_t checkpoint_every, int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk,
     kda_dtype_t in, kda_dtype_t out, void* workspace, size_t workspace_bytes, void* stream) {
   const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
-                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk)
                           : kChunk;
   return chunk_fwd_impl(q, k, v, a, beta, initial_state, o, final_state, checkpoints,
                         checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
@@ -492,7 +493,7 @@ extern "C" kda_status_t kda_chunk_fwd_output_gate(
     kda_dtype_t in, kda_dtype_t out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!gate) return KDA_ERR_NULL;
   const int64_t seg = sizes_ok(B, T, H, dk, dv, chunk, in)
-                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16)
+                          ? auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk)
                           : kChunk;
   return chunk_fwd_impl(q, k, v, g, beta, initial_state, o, final_state, checkpoints,
                         checkpoint_every, B, T, H, dk, dv, chunk, in, out, seg, workspace,
@@ -534,7 +535,7 @@ extern "C" kda_status_t kda_chunk_fwd_noalloc(const void* q, const void* k, cons
                                               int64_t H, int dk, int dv, int chunk,
                                               kda_dtype_t in, kda_dtype_t out, void* stream) {
   if (!sizes_ok(B, T, H, dk, dv, chunk, in)) return KDA_ERR_SHAPE;
-  const int64_t seg = auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16);
+  const int64_t seg = auto_segment_tokens(B, T, H, dk, dv, in == KDA_BF16, chunk);
   const int64_t nseg = num_segments(T, seg);
   if (!mul_ok(B * H, nseg) || !mul_ok(B * H * nseg, (int64_t)dk * (2 * dv + dk) * 4))
     return KDA_ERR_SHAPE;
