@@ -41,6 +41,12 @@
 //   substitution for U (four waves), P to hi / lo rows (four waves) | P U,
 //   output tile, state update | output stores, next chunk's inputs to shared
 //   memory.
+//
+// The walk itself is in kda_prefill_body.inc, one text used twice: inside the
+// ordinary kernel (chunk_fwd_kernel) and inside a device function (chunk_body)
+// that the segmented path's summary kernel calls for its two kinds of workgroup.
+// Its summary variant (SUM) drops the query, P-tile and output work, which frees
+// the shared memory for all 128 value columns in one workgroup.
 
 #include <type_traits>
 
